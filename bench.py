@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X skinny GEMM (C = A . B^T, bf16, M <= 16).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--points-out FILE]
+
+One step = one call of the GEMM for every (M, K, N) point of the workload, in
+order, each on its own synthetic inputs already resident in HBM.  The weight
+matrix of every call is one of several byte-identical copies at different
+addresses, cycled so that the bytes touched between two uses of a copy exceed
+the 256 MB Infinity Cache: every call reads its weights from HBM.
+
+Prints ONE JSON line:
+  value        = sum over the step's calls of the weight bytes 2*N*K, divided
+                 by the measured time per step (GB/s, whole GPU);
+  roofline     = the dominant kernel (the point with the largest time in the
+                 step): algorithmic bytes per launch (2NK + 2MK + M*N*s_out)
+                 divided by its average launch duration, timed with HIP events
+                 around each of its launches inside the timed region;
+  cpu_baseline = the CPU oracle timed on this host over the same workload.
+``--points-out`` also writes per-point microseconds per call for every
+workload point (eager launches and HIP-graph replay) as JSON.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (weight read) and µs/call, bf16 skinny GEMM, M=1..16"
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30  # footprint between two uses of one weight copy
+DEFAULT_WORKLOAD = "wide_deep"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
+                  "skg_valu_hi.hip", "skg_api.cpp", "tuned_table.inc"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "latency_decode_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--points-out", default=None,
+                    help="write per-point us/call for all 29 points to this JSON file")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", default=None,
+                    help="profile helper: run only the point 'M,K,N' (no JSON checks)")
+    return ap.parse_args()
+
+
+class Point:
+    """Device buffers of one workload point (A, rotating B copies, C)."""
+
+    def __init__(self, torch, skg, inputs, p, b_pool):
+        self.M, self.K, self.N = p["M"], p["K"], p["N"]
+        self.out = p["out"]
+        self.ldc = p["ldc"] or self.N
+        self.A_bits = inputs.make_a(self.M, self.K, self.N)
+        self.A = torch.from_numpy(self.A_bits.view("int16")).cuda().view(torch.bfloat16)
+        self.copies = b_pool[(self.K, self.N)]
+        dt = torch.bfloat16 if self.out == "bf16" else torch.float32
+        self.Cbuf = torch.zeros((self.M, self.ldc), dtype=dt, device="cuda")
+        self.odt = skg.SKG_OUT_BF16 if self.out == "bf16" else skg.SKG_OUT_F32
+        self.cfg = skg.skinny_gemm_dispatch(self.M, self.K, self.N)
+        self.s_out = 2 if self.out == "bf16" else 4
+        self.weight_bytes = 2 * self.N * self.K
+        self.alg_bytes = 2 * self.N * self.K + 2 * self.M * self.K + self.M * self.N * self.s_out
+
+    def name(self):
+        return f"M{self.M}_K{self.K}_N{self.N}_{self.out}" + (
+            f"_ldc{self.ldc}" if self.ldc != self.N else "")
+
+
+class BPool:
+    """Per (K, N): the seeded weights and byte-identical copies of them."""
+
+    def __init__(self, torch, inputs, shapes, rotate_bytes=ROTATE_BYTES):
+        self.torch = torch
+        self.bits = {}
+        self.copies = {}
+        for (K, N) in shapes:
+            bits = inputs.make_b(K, N)
+            self.bits[(K, N)] = bits
+            base = torch.from_numpy(bits.view("int16")).cuda().view(torch.bfloat16)
+            n = max(2, math.ceil(rotate_bytes / (2 * N * K)))
+            lst = [base] + [base.clone() for _ in range(n - 1)]
+            self.copies[(K, N)] = {"list": lst, "next": 0}
+
+    def __getitem__(self, key):
+        return self.copies[key]
+
+
+def call(lib, pt, B, stream_handle):
+    st = lib.skinny_gemm_bf16(pt.A.data_ptr(), B.data_ptr(), pt.Cbuf.data_ptr(), pt.M, pt.N,
+                              pt.K, pt.K, pt.K, pt.ldc, pt.odt, stream_handle)
+    if st != 0:
+        raise RuntimeError(f"skinny_gemm_bf16 failed for {pt.name()}: status {st}")
+
+
+def next_copy(pt):
+    c = pt.copies
+    B = c["list"][c["next"]]
+    c["next"] = (c["next"] + 1) % len(c["list"])
+    return B
+
+
+def check_parity(oracle, acceptance, pt, bits_B, torch):
+    """Sampled outputs against the oracle (all M rows, up to 64 columns)."""
+    import numpy as np
+    C = pt.Cbuf[:, :pt.N].float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(0)
+    ns = np.sort(rng.choice(pt.N, size=min(64, pt.N), replace=False))
+    ms = np.repeat(np.arange(pt.M), ns.size)
+    nn = np.tile(ns, pt.M)
+    ref = oracle.gemm_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
+    an = acceptance.row_norms(oracle.bf16_decode(pt.A_bits), pt.K)
+    bn = acceptance.row_norms(oracle.bf16_decode(bits_B[ns]), pt.K)
+    return acceptance.assess(C[:, ns], ref, an, bn, pt.out)
+
+
+def time_points_graph(torch, lib, pts, stream, calls=200, warm=20):
+    """us per call of each point: back-to-back calls replayed from a HIP graph
+    (rotating weight copies), so host launch cost is excluded."""
+    res = {}
+    h = stream.cuda_stream
+    for pt in pts:
+        for _ in range(warm):
+            call(lib, pt, next_copy(pt), h)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        n = min(calls, 4 * len(pt.copies["list"])) if pt.weight_bytes > (64 << 20) else calls
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                call(lib, pt, next_copy(pt), stream.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / n
+        res[pt.name()] = us
+        del g
+    return res
+
+
+def time_points_eager(torch, lib, pts, stream, calls=200, warm=20):
+    res = {}
+    h = stream.cuda_stream
+    for pt in pts:
+        for _ in range(warm):
+            call(lib, pt, next_copy(pt), h)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            for _ in range(calls):
+                call(lib, pt, next_copy(pt), h)
+            e1.record()
+        torch.cuda.synchronize()
+        res[pt.name()] = e0.elapsed_time(e1) * 1000.0 / calls
+    return res
+
+
+def cpu_baseline(oracle, pts, bpool, budget_s):
+    """The oracle over the whole workload (every output), repeated up to the
+    time budget; rate = weight bytes per second."""
+    threads = oracle.default_threads()
+    passes, t_total, bytes_total = 0, 0.0, 0
+    t_start = time.time()
+    while passes < 3 and (passes == 0 or time.time() - t_start < budget_s):
+        for pt in pts:
+            t0 = time.perf_counter()
+            oracle.gemm_f64(pt.A_bits, bpool.bits[(pt.K, pt.N)], pt.K, threads=threads)
+            t_total += time.perf_counter() - t0
+            bytes_total += pt.weight_bytes
+        passes += 1
+    return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole workload ({len(pts)} calls, every output), {passes} pass(es), "
+                      f"{t_total:.1f} s; binary64 C loop, OpenMP over columns"}
+
+
+def load_traffic(dominant_name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("points", {}).get(dominant_name)
+    if not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of this GEMM is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import latency_decode_gemm_amd as skg
+    from latency_decode_gemm_amd import _capi, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lib = _capi.lib()
+    if not skg.skinny_gemm_available():
+        print("bench.py: libskinny_gemm.so has no gfx950 device/code to run", file=sys.stderr)
+        sys.exit(1)
+
+    workload = inputs.WORKLOADS[args.workload]
+    if args.only:
+        M, K, N = (int(x) for x in args.only.split(","))
+        workload = [p for p in inputs.all_points() if (p["M"], p["K"], p["N"]) == (M, K, N)]
+    shapes = list(dict.fromkeys((p["K"], p["N"]) for p in workload))
+    ms = sorted(set(p["M"] for p in workload))
+    bpool = BPool(torch, inputs, shapes)
+    pts = [Point(torch, skg, inputs, p, bpool) for p in workload]
+    # all work on one non-default stream (graph capture needs one)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    h = stream.cuda_stream
+    skg.skinny_gemm_warmup(shapes, ms, stream=stream)
+
+    # untimed warm-up steps; also find the dominant point (largest time per call)
+    for _ in range(max(args.warmup, 1)):
+        for pt in pts:
+            call(lib, pt, next_copy(pt), h)
+    torch.cuda.synchronize()
+    probe = time_points_eager(torch, lib, pts, stream, calls=20, warm=2)
+    dom = max(pts, key=lambda p: probe[p.name()])
+
+    # timed region: K steps; HIP events around each launch of the dominant point
+    n_dom = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_dom)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_dom)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(args.steps):
+        for pt in pts:
+            B = next_copy(pt)
+            if pt is dom:
+                ev_s[s].record()
+                call(lib, pt, B, h)
+                ev_e[s].record()
+            else:
+                call(lib, pt, B, h)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+    weight_bytes_step = sum(p.weight_bytes for p in pts)
+    value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
+    dom_us = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])) * 1000.0
+    achieved = dom.alg_bytes / (dom_us * 1e-6) / 1e9
+
+    # results are still right after the timed loop (sampled oracle check)
+    bad = []
+    if not args.only:
+        import oracle
+        from oracle import acceptance
+        for pt in pts:
+            r = check_parity(oracle, acceptance, pt, bpool.bits[(pt.K, pt.N)], torch)
+            if not r["ok"]:
+                bad.append((pt.name(), r))
+    if bad:
+        print(f"bench.py: results do not match the oracle: {bad}", file=sys.stderr)
+        sys.exit(1)
+
+    traffic = load_traffic(dom.name())
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic,
+                "kernel": dom.name(), "launch_us": round(dom_us, 3),
+                "alg_bytes_per_launch": dom.alg_bytes,
+                "config": dom.cfg.as_dict()}
+    per_point = {p.name(): round(probe[p.name()], 3) for p in pts}
+    cpu = None
+    if not args.no_cpu and not args.only:
+        import oracle
+        cpu = cpu_baseline(oracle, pts, bpool, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload + ": " + ", ".join(p.name() for p in pts),
+                   "accumulate": "f32", "weight_bytes_per_step": weight_bytes_step,
+                   "parallelism": "single GPU", "weight_copies_rotated": True,
+                   "host_wall_s": round(wall, 3)},
+        "us_per_call_eager": per_point,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if args.points_out:
+        all_pts_spec = inputs.all_points()
+        shapes_all = list(dict.fromkeys((p["K"], p["N"]) for p in all_pts_spec))
+        del pts, bpool
+        torch.cuda.empty_cache()
+        table = {}
+        for (K, N) in shapes_all:
+            sub = [p for p in all_pts_spec if (p["K"], p["N"]) == (K, N)]
+            bp = BPool(torch, inputs, [(K, N)])
+            ps = [Point(torch, skg, inputs, p, bp) for p in sub]
+            skg.skinny_gemm_warmup([(K, N)], [p.M for p in ps], stream=stream)
+            eager = time_points_eager(torch, lib, ps, stream)
+            graph = time_points_graph(torch, lib, ps, stream)
+            hot = BPool(torch, inputs, [(K, N)], rotate_bytes=0)
+            for p in ps:
+                p.copies = hot[(K, N)]
+                p.copies["list"] = p.copies["list"][:1]
+            hot_us = time_points_graph(torch, lib, ps, stream)
+            for p in ps:
+                nm = p.name()
+                table[nm] = {"M": p.M, "K": p.K, "N": p.N, "out": p.out, "ldc": p.ldc,
+                             "config": p.cfg.as_dict(),
+                             "us_per_call_eager": round(eager[nm], 3),
+                             "us_per_call_graph": round(graph[nm], 3),
+                             "weight_GBps_graph": round(p.weight_bytes / graph[nm] / 1e3, 1),
+                             "frac_of_8TBps_graph": round(p.weight_bytes / graph[nm] / 1e3 / PEAK_HBM_GBS, 4),
+                             "us_per_call_hot_graph": round(hot_us[nm], 3)}
+            del ps, bp, hot
+            torch.cuda.empty_cache()
+        with open(args.points_out, "w") as f:
+            json.dump(table, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

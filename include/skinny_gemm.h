@@ -1,0 +1,163 @@
+/*
+ * skinny_gemm.h -- C ABI of the MI355X (gfx950) small-M bf16 "skinny" GEMM.
+ *
+ *     C[m, n] = sum_k A[m, k] * B[n, k]          (C = A . B^T, M <= 16)
+ *
+ * A (activations, M x K) and B (weights, N x K) are row-major bf16; the sum
+ * is accumulated in fp32; C is written as fp32 or as bf16 (round to nearest
+ * even), optionally into a strided buffer.
+ *
+ * Sources on the pages:
+ *   - PR #42562 page ("Add generic cuteDSL LL BF16 router (GEMM)"):
+ *     section 实现拆解 item 1 (dot-product kernel: one block per row of B,
+ *     128-bit loads, shuffle + shared-memory reduction, for small M or
+ *     K < 2048), item 2 (split-K kernel: K spread over several blocks whose
+ *     partial sums are combined), item 3 (dispatch on M, K, N and a cache of
+ *     built kernels, plus a warm-up key list), item 4 (the router gate uses it
+ *     only when M <= 16 and the activations are bf16; the review section
+ *     评论区精华 adds the weight-dtype guard, the 16-byte alignment of 128-bit
+ *     loads and the unsupported non-fp32 output); ll_bf16.py excerpt under
+ *     关键源码片段 (dispatch and get_warmup_keys).
+ *   - PR #48597 page ("GLM-5.2 Blackwell decode optimizations"), section
+ *     实现拆解 item 3 and the key-file list: bf16_skinny_gemm for the qkv_a /
+ *     q_b / eh_proj decode projections, with a strided-output test.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers A, B, C are DEVICE pointers owned by the caller; the library
+ *     never frees or retains them beyond the call's stream work.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; no entry point synchronises the host
+ *     except skinny_gemm_warmup (which waits for its own launches).
+ *   - Strides lda, ldb, ldc are in ELEMENTS.  Element (m, k) of A lives at
+ *     A[m*lda + k], (n, k) of B at B[n*ldb + k], (m, n) of C at C[m*ldc + n].
+ *     Every other element of the C buffer is left untouched.
+ *   - Every function returns an skg_status and never aborts.  Argument
+ *     checks run on the host before any HIP call, so an error return leaves
+ *     device memory unchanged.
+ *   - Thread safety: all entry points may be called from several host
+ *     threads.  Calls on different streams use different workspaces; calls
+ *     on one stream are ordered by the stream.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SKG_OK = 0,
+    SKG_ERR_INVALID_ARG = 1, /* null pointer with non-zero size, negative size,
+                                lda < K, ldb < K, ldc < N, bad out_dtype, bad config */
+    SKG_ERR_UNSUPPORTED = 2, /* M > 16: the caller should use another GEMM */
+    SKG_ERR_MISALIGNED = 3,  /* A or B not 16-byte aligned, lda or ldb not a
+                                multiple of 8, C not aligned to its element size */
+    SKG_ERR_NOT_WARMED = 4,  /* the stream is capturing a graph and its split-K
+                                workspace is too small: warm up first */
+    SKG_ERR_HIP = 5,         /* a HIP runtime call or a kernel launch failed */
+    SKG_ERR_NO_DEVICE = 6    /* no gfx950 device / the code object does not load */
+} skg_status;
+
+typedef enum { SKG_OUT_F32 = 0, SKG_OUT_BF16 = 1 } skg_out_dtype;
+
+typedef enum {
+    SKG_BACKEND_DOT = 0,   /* one workgroup per block of rows of B covers all of K */
+    SKG_BACKEND_SPLITK = 1 /* split_k workgroups per row block, each one slice of K;
+                              fp32 partials are summed in a fixed order by the
+                              last workgroup to finish (no spin-wait) */
+} skg_backend;
+
+typedef enum {
+    SKG_INNER_VALU = 0, /* bf16 dot2 instructions, 16 lanes per row of B */
+    SKG_INNER_MFMA = 1  /* 16x16x32 bf16 matrix-core tiles (M padded to 16) */
+} skg_inner;
+
+#define SKG_MAX_M 16
+
+/* A kernel configuration: what skinny_gemm_dispatch returns and what
+ * skinny_gemm_bf16_with_config accepts.  Plain data; compare field by field. */
+typedef struct skg_config {
+    int32_t backend;   /* skg_backend; SKG_BACKEND_DOT requires split_k == 1,
+                          SKG_BACKEND_SPLITK requires split_k >= 2 */
+    int32_t inner;     /* skg_inner */
+    int32_t split_k;   /* workgroups along K per row block */
+    int32_t row_tiles; /* rows per wave: VALU 4*row_tiles (1, 2, 4);
+                          MFMA 16*row_tiles (1, 2, 4) */
+    int32_t waves_n;   /* waves per workgroup on different rows */
+    int32_t waves_k;   /* waves per workgroup on different K slices of the same
+                          rows (combined through LDS); waves_n*waves_k <= 16 */
+    int32_t depth;     /* K steps of B loads kept in flight per wave
+                          (VALU: 2, 4, 8; MFMA: 2, 4, 8; see skinny_gemm_check_config) */
+} skg_config;
+
+/*
+ * C = A . B^T with the configuration skinny_gemm_dispatch(M, K, N) returns.
+ *   A: device bf16 [M, lda], 16-byte aligned, lda % 8 == 0, lda >= K.
+ *   B: device bf16 [N, ldb], 16-byte aligned, ldb % 8 == 0, ldb >= K.
+ *   C: device [M, ldc] of fp32 (out_dtype SKG_OUT_F32, 4-byte aligned) or
+ *      bf16 (SKG_OUT_BF16, 2-byte aligned, round to nearest even), ldc >= N.
+ *   0 <= M <= 16 (M > 16 -> SKG_ERR_UNSUPPORTED), N >= 0, K >= 0.
+ *   M == 0 or N == 0: nothing is written, SKG_OK.  K == 0: C gets zeros.
+ * The result for a given (M, K, N) and inputs is bit-identical from call to
+ * call (fixed summation order; no floating-point atomics).
+ */
+int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
+                     int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
+                     void *stream);
+
+/* Same as skinny_gemm_bf16 with an explicit configuration (tests, tuning).
+ * An invalid or unsupported configuration returns SKG_ERR_INVALID_ARG. */
+int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M,
+                                 int N, int K, int64_t lda, int64_t ldb,
+                                 int64_t ldc, int out_dtype, void *stream,
+                                 const skg_config *cfg);
+
+/* The configuration used for (M, K, N).  Pure host function: no GPU access,
+ * deterministic, the same answer on every call.  M must be in 1..16,
+ * K >= 0, N >= 1; otherwise SKG_ERR_INVALID_ARG / SKG_ERR_UNSUPPORTED. */
+int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
+
+/* Whether cfg can run (M, K, N): SKG_OK or SKG_ERR_INVALID_ARG.  Pure host. */
+int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg);
+
+/* Bytes of split-K workspace (partials + tickets) cfg needs for (M, K, N);
+ * 0 for SKG_BACKEND_DOT.  Pure host. */
+int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg,
+                                size_t *bytes);
+
+/*
+ * Warm-up keys: the distinct results of skinny_gemm_dispatch(M, K, N) for
+ * every (K, N) in kn_pairs (n_shapes pairs, laid out K0, N0, K1, N1, ...) and
+ * every M in m_values, in first-seen order (shapes outer, M inner).  Writes at
+ * most `capacity` configs to `out` (may be NULL when capacity is 0) and the
+ * total count to *n_out.  Pure host.
+ */
+int skinny_gemm_warmup_keys(const int *kn_pairs, int n_shapes,
+                            const int *m_values, int n_m, skg_config *out,
+                            int capacity, int *n_out);
+
+/*
+ * Prepares `stream` for every (K, N) x M combination: makes sure the code
+ * object is loaded, sizes this stream's split-K workspace for the largest
+ * combination, and runs each distinct configuration once on a small scratch
+ * problem.  Idempotent.  Allocates device memory and synchronises `stream`;
+ * call it before graph capture.  *n_configs_out (may be NULL) receives the
+ * number of distinct configurations.
+ */
+int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values,
+                       int n_m, void *stream, int *n_configs_out);
+
+/* 1 if a gfx950 device is current and the library's kernels load, else 0. */
+int skinny_gemm_available(void);
+
+/* Static description of a status code. */
+const char *skinny_gemm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

@@ -1,0 +1,118 @@
+"""ctypes declarations for libskinny_gemm.so (see include/skinny_gemm.h).
+
+Loading is lazy and loud: the first call that needs the library raises
+``RuntimeError`` if ``libskinny_gemm.so`` has not been built.  There is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskinny_gemm.so")
+
+SKG_OK = 0
+SKG_ERR_INVALID_ARG = 1
+SKG_ERR_UNSUPPORTED = 2
+SKG_ERR_MISALIGNED = 3
+SKG_ERR_NOT_WARMED = 4
+SKG_ERR_HIP = 5
+SKG_ERR_NO_DEVICE = 6
+
+SKG_OUT_F32 = 0
+SKG_OUT_BF16 = 1
+
+SKG_BACKEND_DOT = 0
+SKG_BACKEND_SPLITK = 1
+SKG_INNER_VALU = 0
+SKG_INNER_MFMA = 1
+SKG_MAX_M = 16
+
+# Every function the header declares, with (restype, argtypes).
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_ip = ctypes.POINTER(ctypes.c_int)
+
+
+class SkgConfig(ctypes.Structure):
+    """Mirror of ``skg_config``."""
+    _fields_ = [("backend", ctypes.c_int32), ("inner", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
+                ("depth", ctypes.c_int32)]
+
+    FIELDS = ("backend", "inner", "split_k", "row_tiles", "waves_n", "waves_k", "depth")
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f in self.FIELDS)
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f in self.FIELDS}
+
+    @classmethod
+    def make(cls, backend=None, inner=SKG_INNER_VALU, split_k=1, row_tiles=1, waves_n=1,
+             waves_k=1, depth=4):
+        if backend is None:
+            backend = SKG_BACKEND_DOT if split_k == 1 else SKG_BACKEND_SPLITK
+        return cls(backend, inner, split_k, row_tiles, waves_n, waves_k, depth)
+
+    def __eq__(self, other):
+        return isinstance(other, SkgConfig) and self.as_tuple() == other.as_tuple()
+
+    def __hash__(self):
+        return hash(self.as_tuple())
+
+    def __repr__(self):
+        return "SkgConfig(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
+
+
+_cfgp = ctypes.POINTER(SkgConfig)
+
+SIGNATURES = {
+    "skinny_gemm_bf16": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp]),
+    "skinny_gemm_bf16_with_config": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i,
+                                          _vp, _cfgp]),
+    "skinny_gemm_dispatch": (_i, [_i, _i, _i, _cfgp]),
+    "skinny_gemm_check_config": (_i, [_i, _i, _i, _cfgp]),
+    "skinny_gemm_workspace_bytes": (_i, [_i, _i, _i, _cfgp, ctypes.POINTER(ctypes.c_size_t)]),
+    "skinny_gemm_warmup_keys": (_i, [_ip, _i, _ip, _i, _cfgp, _i, _ip]),
+    "skinny_gemm_warmup": (_i, [_ip, _i, _ip, _i, _vp, _ip]),
+    "skinny_gemm_available": (_i, []),
+    "skinny_gemm_strerror": (ctypes.c_char_p, [_i]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m latency_decode_gemm_amd.build` (there is no fallback)")
+                dll = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(dll, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = dll
+    return _lib
+
+
+class SkinnyGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().skinny_gemm_strerror(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def check(status: int, where: str) -> None:
+    if status != SKG_OK:
+        raise SkinnyGemmError(status, where)

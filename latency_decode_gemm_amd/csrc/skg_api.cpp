@@ -1,0 +1,426 @@
+// skg_api.cpp -- C ABI of the skinny GEMM: argument checks, dispatch,
+// launch geometry, per-stream split-K workspace, warm-up.
+//
+// Dispatch follows the shape-keyed selection on the PR #42562 page
+// ("Add generic cuteDSL LL BF16 router (GEMM)", section 实现拆解 item 3 and
+// the ll_bf16.py excerpt): a pure function of (M, K, N) that looks up a table
+// tuned per (K, N) and M and otherwise falls back to a default.  Here the table
+// is compiled in (tuned_table.inc, measured on MI355X) and returns a complete
+// skg_config; there is no runtime switch that changes the choice.  The
+// warm-up key list keeps the first-seen order of the distinct configurations,
+// as get_warmup_keys does on that page.
+//
+// Eligibility mirrors the router gate of the same page (item 4 and the
+// review section 评论区精华): M <= 16, bf16 operands, 16-byte aligned 128-bit
+// loads; anything else is rejected with a status code so the caller can fall
+// back to another GEMM.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "skg_internal.h"
+
+namespace skg {
+
+namespace {
+
+struct TableEntry {
+    int M, K, N;
+    skg_config cfg;
+};
+
+#include "tuned_table.inc"
+
+constexpr int kNumTable = sizeof(kTunedTable) / sizeof(kTunedTable[0]);
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+int round_up(int a, int b) { return ceil_div(a, b) * b; }
+
+bool config_equal(const skg_config &a, const skg_config &b) {
+    return a.backend == b.backend && a.inner == b.inner && a.split_k == b.split_k &&
+           a.row_tiles == b.row_tiles && a.waves_n == b.waves_n && a.waves_k == b.waves_k &&
+           a.depth == b.depth;
+}
+
+// Default for shapes the table does not list: VALU up to M = 8, MFMA above;
+// enough workgroups to cover the 256 CUs a few times over; A slice <= 64 KB.
+skg_config default_config(int M, int K, int N) {
+    skg_config c;
+    std::memset(&c, 0, sizeof c);
+    c.inner = (M > 8) ? SKG_INNER_MFMA : SKG_INNER_VALU;
+    c.row_tiles = (c.inner == SKG_INNER_MFMA) ? 1 : (M <= 2 ? 1 : 2);
+    c.depth = 4;
+    c.waves_n = 1;
+    c.waves_k = 4;
+    const int rows_per_wg = (c.inner == SKG_INNER_MFMA ? 16 : 4 * c.row_tiles) * c.waves_n;
+    const int num_rb = ceil_div(std::max(N, 1), rows_per_wg);
+    const int nck = ceil_div(K, kChunk);
+    const int step = (c.inner == SKG_INNER_MFMA) ? kMfmaStep : kValuStep;
+    int S = 1;
+    // keep the staged A slice within 64 KB and aim for >= 512 workgroups
+    while (S < 16 && (int64_t)M * ceil_div(nck, S) * kChunk * 2 > 64 * 1024) S *= 2;
+    while (S < 16 && num_rb * S < 512 && ceil_div(nck, 2 * S) >= step * c.waves_k) S *= 2;
+    c.split_k = S;
+    c.backend = (S > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
+    Geometry g;
+    // back off until the geometry is valid (an empty last split, LDS size)
+    while (c.split_k > 1 && !make_geometry(M, K, N, c, &g)) {
+        c.split_k /= 2;
+        c.backend = (c.split_k > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
+    }
+    while (!make_geometry(M, K, N, c, &g) && c.waves_k > 1) c.waves_k /= 2;
+    return c;
+}
+
+struct Workspace {
+    float *ws = nullptr;
+    size_t ws_floats = 0;
+    unsigned *tickets = nullptr;
+    size_t n_tickets = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, void *>, Workspace> g_ws;
+
+// The split-K workspace of (current device, stream), grown if needed.
+// Growing is refused while the stream is capturing a graph.
+int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, Workspace *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace &w = g_ws[std::make_pair(dev, (void *)stream)];
+    if (w.ws_floats >= need_floats && w.n_tickets >= need_tickets) {
+        *out = w;
+        return SKG_OK;
+    }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SKG_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return SKG_ERR_NOT_WARMED;
+    // earlier kernels on this stream may still use the old buffers
+    if (hipStreamSynchronize(stream) != hipSuccess) return SKG_ERR_HIP;
+    const size_t nf = std::max(need_floats, w.ws_floats);
+    const size_t nt = std::max(need_tickets, w.n_tickets);
+    float *ws = nullptr;
+    unsigned *tk = nullptr;
+    if (hipMalloc(&ws, std::max<size_t>(nf, 1) * sizeof(float)) != hipSuccess) return SKG_ERR_HIP;
+    if (hipMalloc(&tk, std::max<size_t>(nt, 1) * sizeof(unsigned)) != hipSuccess) {
+        (void)hipFree(ws);
+        return SKG_ERR_HIP;
+    }
+    if (hipMemset(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(ws);
+        (void)hipFree(tk);
+        return SKG_ERR_HIP;
+    }
+    if (w.ws) (void)hipFree(w.ws);
+    if (w.tickets) (void)hipFree(w.tickets);
+    w.ws = ws;
+    w.ws_floats = nf;
+    w.tickets = tk;
+    w.n_tickets = nt;
+    *out = w;
+    return SKG_OK;
+}
+
+int check_args(const void *A, const void *B, const void *C, int M, int N, int K, int64_t lda,
+               int64_t ldb, int64_t ldc, int out_dtype) {
+    if (M < 0 || N < 0 || K < 0) return SKG_ERR_INVALID_ARG;
+    if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
+    if (out_dtype != SKG_OUT_F32 && out_dtype != SKG_OUT_BF16) return SKG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return SKG_OK;
+    if (lda < K || ldb < K || ldc < N) return SKG_ERR_INVALID_ARG;
+    if (C == nullptr) return SKG_ERR_INVALID_ARG;
+    if (K > 0 && (A == nullptr || B == nullptr)) return SKG_ERR_INVALID_ARG;
+    if (K > 0) {
+        if ((reinterpret_cast<uintptr_t>(A) & 15u) || (reinterpret_cast<uintptr_t>(B) & 15u))
+            return SKG_ERR_MISALIGNED;
+        if ((lda & 7) || (ldb & 7)) return SKG_ERR_MISALIGNED;
+    }
+    const uintptr_t csz = (out_dtype == SKG_OUT_F32) ? 4u : 2u;
+    if (reinterpret_cast<uintptr_t>(C) & (csz - 1)) return SKG_ERR_MISALIGNED;
+    return SKG_OK;
+}
+
+int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda, int64_t ldb,
+        int64_t ldc, int out_dtype, void *stream_v, const skg_config &cfg) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (K == 0) {
+        return launch_zero_fill(C, M, N, ldc, out_dtype == SKG_OUT_BF16, stream) == hipSuccess
+                   ? SKG_OK
+                   : SKG_ERR_HIP;
+    }
+    Geometry g;
+    if (!make_geometry(M, K, N, cfg, &g)) return SKG_ERR_INVALID_ARG;
+    KParams p;
+    std::memset(&p, 0, sizeof p);
+    p.A = reinterpret_cast<const uint16_t *>(A);
+    p.B = reinterpret_cast<const uint16_t *>(B);
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.out_bf16 = (out_dtype == SKG_OUT_BF16);
+    p.nck = g.nck;
+    p.nfull = g.nfull;
+    p.split_k = cfg.split_k;
+    p.wg_chunks = g.wg_chunks;
+    p.wave_chunks = g.wave_chunks;
+    p.waves_n = cfg.waves_n;
+    p.waves_k = cfg.waves_k;
+    p.rows_per_wg = g.rows_per_wg;
+    p.num_rb = g.num_rb;
+    p.lds_stride = g.lds_stride;
+    p.red_offset = g.red_offset;
+    if (cfg.split_k > 1) {
+        Workspace w;
+        const int st = get_workspace(stream, g.ws_floats, g.n_tickets, &w);
+        if (st != SKG_OK) return st;
+        p.ws = w.ws;
+        p.tickets = w.tickets;
+    }
+    return launch(p, g, cfg, stream) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
+}
+
+}  // namespace
+
+bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
+    if (M < 1 || M > SKG_MAX_M || K < 0 || N < 1) return false;
+    if (cfg.backend == SKG_BACKEND_DOT) {
+        if (cfg.split_k != 1) return false;
+    } else if (cfg.backend == SKG_BACKEND_SPLITK) {
+        if (cfg.split_k < 2 || cfg.split_k > 4096) return false;
+    } else {
+        return false;
+    }
+    if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA) return false;
+    if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth)) return false;
+    if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
+    Geometry r;
+    r.step = (cfg.inner == SKG_INNER_VALU) ? kValuStep : kMfmaStep;
+    r.nck = ceil_div(K, kChunk);
+    r.nfull = K / kChunk;
+    r.rows_per_wave = (cfg.inner == SKG_INNER_VALU) ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
+    r.rows_per_wg = r.rows_per_wave * cfg.waves_n;
+    r.num_rb = ceil_div(N, r.rows_per_wg);
+    const int S = cfg.split_k;
+    const int per_split = ceil_div(std::max(r.nck, 1), S);
+    r.wave_chunks = round_up(ceil_div(per_split, cfg.waves_k), r.step);
+    r.wg_chunks = r.wave_chunks * cfg.waves_k;
+    if ((int64_t)(S - 1) * r.wg_chunks >= std::max(r.nck, 1)) return false;  // empty split
+    r.lds_stride = r.wg_chunks * kChunk + kChunk;
+    const size_t a_bytes = (size_t)M * r.lds_stride * 2;
+    r.red_offset = (int)((a_bytes + 15) / 16 * 16);
+    const size_t red_bytes = (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
+    r.lds_bytes = r.red_offset + red_bytes + 16;
+    if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
+    r.threads = 64 * cfg.waves_n * cfg.waves_k;
+    r.ws_floats = (S > 1) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
+    r.n_tickets = (S > 1) ? (size_t)r.num_rb : 0;
+    if ((int64_t)r.num_rb * S > 0x7FFFFFFF) return false;
+    *g = r;
+    return true;
+}
+
+}  // namespace skg
+
+using namespace skg;
+
+extern "C" {
+
+int skinny_gemm_dispatch(int M, int K, int N, skg_config *out) {
+    if (!out) return SKG_ERR_INVALID_ARG;
+    if (M < 1 || K < 0 || N < 1) return M > SKG_MAX_M ? SKG_ERR_UNSUPPORTED : SKG_ERR_INVALID_ARG;
+    if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
+    for (int i = 0; i < kNumTable; ++i) {
+        const TableEntry &e = kTunedTable[i];
+        if (e.M == M && e.K == K && e.N == N) {
+            Geometry g;
+            if (make_geometry(M, K, N, e.cfg, &g)) {
+                *out = e.cfg;
+                return SKG_OK;
+            }
+        }
+    }
+    *out = default_config(M, K, N);
+    return SKG_OK;
+}
+
+int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg) {
+    if (!cfg) return SKG_ERR_INVALID_ARG;
+    Geometry g;
+    return make_geometry(M, K, N, *cfg, &g) ? SKG_OK : SKG_ERR_INVALID_ARG;
+}
+
+int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg, size_t *bytes) {
+    if (!cfg || !bytes) return SKG_ERR_INVALID_ARG;
+    Geometry g;
+    if (!make_geometry(M, K, N, *cfg, &g)) return SKG_ERR_INVALID_ARG;
+    *bytes = g.ws_floats * sizeof(float) + g.n_tickets * sizeof(unsigned);
+    return SKG_OK;
+}
+
+int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
+                     int64_t ldb, int64_t ldc, int out_dtype, void *stream) {
+    const int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, out_dtype);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    skg_config cfg;
+    const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
+    if (ds != SKG_OK) return ds;
+    return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg);
+}
+
+int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M, int N, int K,
+                                 int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
+                                 void *stream, const skg_config *cfg) {
+    if (!cfg) return SKG_ERR_INVALID_ARG;
+    const int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, out_dtype);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    Geometry g;
+    if (K > 0 && !make_geometry(M, K, N, *cfg, &g)) return SKG_ERR_INVALID_ARG;
+    return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, *cfg);
+}
+
+int skinny_gemm_warmup_keys(const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
+                            skg_config *out, int capacity, int *n_out) {
+    if (n_shapes < 0 || n_m < 0 || capacity < 0 || !n_out) return SKG_ERR_INVALID_ARG;
+    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values) || (capacity > 0 && !out))
+        return SKG_ERR_INVALID_ARG;
+    std::vector<skg_config> keys;
+    for (int i = 0; i < n_shapes; ++i) {
+        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
+        for (int j = 0; j < n_m; ++j) {
+            skg_config c;
+            const int st = skinny_gemm_dispatch(m_values[j], K, N, &c);
+            if (st != SKG_OK) return st;
+            bool seen = false;
+            for (const skg_config &k : keys) seen = seen || config_equal(k, c);
+            if (!seen) keys.push_back(c);
+        }
+    }
+    for (int i = 0; i < (int)keys.size() && i < capacity; ++i) out[i] = keys[i];
+    *n_out = (int)keys.size();
+    return SKG_OK;
+}
+
+int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
+                       void *stream_v, int *n_configs_out) {
+    if (n_shapes < 0 || n_m < 0) return SKG_ERR_INVALID_ARG;
+    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values)) return SKG_ERR_INVALID_ARG;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    // the distinct configurations, the workspace they need, and a scratch
+    // problem large enough to run each of them once
+    std::vector<std::pair<skg_config, std::pair<int, int>>> todo;  // cfg, (M, K)
+    size_t need_f = 0, need_t = 0, max_a = 0, max_b = 0, max_c = 0;
+    for (int i = 0; i < n_shapes; ++i) {
+        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
+        if (K < 0 || N < 1) return SKG_ERR_INVALID_ARG;
+        for (int j = 0; j < n_m; ++j) {
+            const int M = m_values[j];
+            skg_config c;
+            const int st = skinny_gemm_dispatch(M, K, N, &c);
+            if (st != SKG_OK) return st;
+            if (K == 0) continue;
+            Geometry g;
+            if (!make_geometry(M, K, N, c, &g)) return SKG_ERR_INVALID_ARG;
+            need_f = std::max(need_f, g.ws_floats);
+            need_t = std::max(need_t, g.n_tickets);
+            bool seen = false;
+            for (auto &t : todo)
+                seen = seen || (config_equal(t.first, c) && t.second.first == M &&
+                                t.second.second == K);
+            if (!seen) {
+                todo.push_back({c, {M, K}});
+                const size_t rows = (size_t)g.rows_per_wg;
+                const size_t ld = (size_t)round_up(K, kChunk);
+                max_a = std::max(max_a, (size_t)M * ld);
+                max_b = std::max(max_b, rows * ld);
+                max_c = std::max(max_c, (size_t)M * rows);
+            }
+        }
+    }
+    int nd = 0;
+    {
+        std::vector<skg_config> uniq;
+        for (auto &t : todo) {
+            bool seen = false;
+            for (auto &u : uniq) seen = seen || config_equal(u, t.first);
+            if (!seen) uniq.push_back(t.first);
+        }
+        nd = (int)uniq.size();
+    }
+    if (n_configs_out) *n_configs_out = nd;
+    if (todo.empty()) return SKG_OK;
+    if (need_f > 0 || need_t > 0) {
+        Workspace w;
+        const int st = get_workspace(stream, need_f, need_t, &w);
+        if (st != SKG_OK) return st;
+    }
+    uint16_t *a = nullptr, *b = nullptr;
+    float *c = nullptr;
+    if (hipMalloc(&a, max_a * 2) != hipSuccess) return SKG_ERR_HIP;
+    if (hipMalloc(&b, max_b * 2) != hipSuccess) {
+        (void)hipFree(a);
+        return SKG_ERR_HIP;
+    }
+    if (hipMalloc(&c, max_c * 4) != hipSuccess) {
+        (void)hipFree(a);
+        (void)hipFree(b);
+        return SKG_ERR_HIP;
+    }
+    int rc = SKG_OK;
+    if (hipMemsetAsync(a, 0, max_a * 2, stream) != hipSuccess ||
+        hipMemsetAsync(b, 0, max_b * 2, stream) != hipSuccess)
+        rc = SKG_ERR_HIP;
+    for (auto &t : todo) {
+        if (rc != SKG_OK) break;
+        const int M = t.second.first, K = t.second.second;
+        Geometry g;
+        make_geometry(M, K, 1, t.first, &g);
+        const int ld = round_up(K, kChunk);
+        rc = run(a, b, c, M, g.rows_per_wg, K, ld, ld, g.rows_per_wg, SKG_OUT_F32, stream,
+                 t.first);
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess && rc == SKG_OK) rc = SKG_ERR_HIP;
+    (void)hipFree(a);
+    (void)hipFree(b);
+    (void)hipFree(c);
+    return rc;
+}
+
+int skinny_gemm_available(void) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return 0;
+    return probe_kernels() == hipSuccess ? 1 : 0;
+}
+
+const char *skinny_gemm_strerror(int status) {
+    switch (status) {
+        case SKG_OK: return "success";
+        case SKG_ERR_INVALID_ARG: return "invalid argument";
+        case SKG_ERR_UNSUPPORTED: return "unsupported shape (M > 16): use another GEMM";
+        case SKG_ERR_MISALIGNED:
+            return "misaligned operand: A and B need 16-byte alignment and lda, ldb multiples of 8";
+        case SKG_ERR_NOT_WARMED:
+            return "stream is capturing and its split-K workspace is too small: warm up first";
+        case SKG_ERR_HIP: return "HIP runtime error";
+        case SKG_ERR_NO_DEVICE: return "no gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal interface between the C-ABI layer (skg_api.cpp) and the gfx950
+// kernels (skg_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/skinny_gemm.h"
+
+namespace skg {
+
+// K is walked in chunks of 8 bf16 (one 16-byte load).
+constexpr int kChunk = 8;
+// K-step of one wave, in chunks: VALU = 16 lanes x 1 chunk, MFMA = 4 lane
+// groups x 1 chunk (32 k per 16x16x32 instruction).
+constexpr int kValuStep = 16;
+constexpr int kMfmaStep = 4;
+// gfx950 LDS per workgroup.
+constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
+
+// Everything a kernel needs, passed by value.
+struct KParams {
+    const uint16_t *A;
+    const uint16_t *B;
+    void *C;
+    float *ws;          // split-K partials [num_rb][split_k][M][rows_per_wg]
+    unsigned *tickets;  // split-K arrival counters [num_rb], zero between calls
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int out_bf16;
+    int nck;          // ceil(K / 8)
+    int nfull;        // K / 8 (chunks with all 8 elements inside K)
+    int split_k;      // workgroups along K per row block
+    int wg_chunks;    // chunks per split (multiple of wave_chunks)
+    int wave_chunks;  // chunks per K-wave (multiple of the K-step)
+    int waves_n, waves_k;
+    int rows_per_wg;
+    int num_rb;
+    int lds_stride;   // bf16 elements per staged A row in LDS
+    int red_offset;   // byte offset of the cross-wave reduction area in LDS
+};
+
+// Derived launch geometry for (M, K, N, cfg).
+struct Geometry {
+    int step;          // K-step in chunks
+    int nck, nfull;
+    int wave_chunks, wg_chunks;
+    int rows_per_wave, rows_per_wg, num_rb;
+    int threads;
+    int lds_stride;    // elements
+    size_t lds_bytes;
+    int red_offset;
+    size_t ws_floats;  // split-K partial floats
+    size_t n_tickets;
+};
+
+// Fills g; returns false if cfg cannot run (M, K, N).
+bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g);
+
+// Whether (inner, row_tiles, depth) has a compiled kernel.
+bool variant_exists(int inner, int row_tiles, int depth);
+
+// Enqueues the kernel(s) for p with geometry g on stream.
+hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
+                  hipStream_t stream);
+
+// Zero-fills C[m*ldc + n] for K == 0.
+hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
+                            hipStream_t stream);
+
+// Loads a kernel's code object (forces lazy loading) for availability checks.
+hipError_t probe_kernels();
+
+// Kernel variants.  VALU (row_tiles R, depth PF) pairs, in table order; the
+// instantiations live in skg_valu_lo.hip (M = 1..8) and skg_valu_hi.hip
+// (M = 9..16), the MFMA ones in skg_launch.hip.
+using KernelPtr = void (*)(KParams);
+constexpr int kValuVariants[][2] = {{1, 4}, {1, 8}, {2, 2}, {2, 4}, {4, 2}, {4, 4}};
+constexpr int kNumValu = sizeof(kValuVariants) / sizeof(kValuVariants[0]);
+KernelPtr valu_kernel_lo(int M, int variant);
+KernelPtr valu_kernel_hi(int M, int variant);
+
+}  // namespace skg

@@ -1,0 +1,78 @@
+// skg_launch.hip -- MFMA kernel instantiations, the zero-fill kernel, and
+// the launch path shared by every variant.
+#include <algorithm>
+
+#include "skg_device.h"
+
+namespace skg {
+
+namespace {
+
+__global__ void skg_zero_fill_kernel(void *C, int M, int N, int64_t ldc, int out_bf16) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(i / N);
+        const int n = (int)(i - (int64_t)m * N);
+        if (out_bf16)
+            reinterpret_cast<uint16_t *>(C)[(int64_t)m * ldc + n] = 0;
+        else
+            reinterpret_cast<float *>(C)[(int64_t)m * ldc + n] = 0.0f;
+    }
+}
+
+struct MfmaVariant {
+    int G, PF;
+    KernelPtr fn;
+};
+const MfmaVariant kMfmaVariants[] = {
+    {1, 2, skg_mfma_kernel<1, 2>}, {1, 4, skg_mfma_kernel<1, 4>}, {1, 8, skg_mfma_kernel<1, 8>},
+    {2, 2, skg_mfma_kernel<2, 2>}, {2, 4, skg_mfma_kernel<2, 4>}, {2, 8, skg_mfma_kernel<2, 8>},
+    {4, 2, skg_mfma_kernel<4, 2>}, {4, 4, skg_mfma_kernel<4, 4>}};
+constexpr int kNumMfma = sizeof(kMfmaVariants) / sizeof(kMfmaVariants[0]);
+
+KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
+    if (inner == SKG_INNER_VALU) {
+        for (int i = 0; i < kNumValu; ++i)
+            if (kValuVariants[i][0] == row_tiles && kValuVariants[i][1] == depth)
+                return M <= 8 ? valu_kernel_lo(M, i) : valu_kernel_hi(M, i);
+        return nullptr;
+    }
+    if (inner == SKG_INNER_MFMA) {
+        for (int i = 0; i < kNumMfma; ++i)
+            if (kMfmaVariants[i].G == row_tiles && kMfmaVariants[i].PF == depth)
+                return kMfmaVariants[i].fn;
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+bool variant_exists(int inner, int row_tiles, int depth) {
+    return find_kernel(inner, 1, row_tiles, depth) != nullptr;
+}
+
+hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
+                  hipStream_t stream) {
+    KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth);
+    if (!fn) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)g.num_rb * (unsigned)cfg.split_k;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(g.threads), g.lds_bytes, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
+                            hipStream_t stream) {
+    const int64_t total = (int64_t)M * N;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(skg_zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, C, M, N, ldc,
+                       out_bf16);
+    return hipGetLastError();
+}
+
+hipError_t probe_kernels() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(skg_zero_fill_kernel));
+}
+
+}  // namespace skg

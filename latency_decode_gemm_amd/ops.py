@@ -1,0 +1,149 @@
+"""Python entry points with the C ABI's names (argument marshalling only).
+
+Tensors are PyTorch device tensors; every computation runs in the HIP
+library.  dtype guards live here because the C ABI takes ``void*``: both
+operands must be bf16 (the router gate on the PR #42562 page, section
+评论区精华, requires bf16 for the activations and for the weight).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Iterable, Optional, Sequence, Tuple
+
+from . import _capi
+from ._capi import SkgConfig, check
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _round8(x: int) -> int:
+    return (x + 7) // 8 * 8
+
+
+def _marshal(A, B, out, out_dtype):
+    torch = _torch()
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError(f"A and B must be torch.bfloat16 (got {A.dtype}, {B.dtype})")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A must be [M, K] and B [N, K]")
+    M, K = A.shape
+    N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A is [{M}, {K}], B is [{N}, {Kb}]")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    if (K > 1 and A.stride(1) != 1 and M > 0) or (K > 1 and B.stride(1) != 1 and N > 0):
+        raise ValueError("rows of A and B must be contiguous (stride 1 along K)")
+    if out is None:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty((M, N), dtype=dt, device=A.device)
+    if out.dim() != 2 or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}]")
+    if out.dtype == torch.float32:
+        odt = _capi.SKG_OUT_F32
+    elif out.dtype == torch.bfloat16:
+        odt = _capi.SKG_OUT_BF16
+    else:
+        raise TypeError(f"out must be float32 or bfloat16 (got {out.dtype})")
+    if N > 1 and out.stride(1) != 1:
+        raise ValueError("rows of out must be contiguous")
+    if out.device != A.device or B.device != A.device:
+        raise ValueError("A, B and out must be on the same device")
+    # a stride is only meaningful when there is a second row
+    lda = A.stride(0) if M > 1 else max(_round8(K), 8)
+    ldb = B.stride(0) if N > 1 else max(_round8(K), 8)
+    ldc = out.stride(0) if M > 1 else max(N, 1)
+    return M, N, K, lda, ldb, ldc, odt, out
+
+
+def skinny_gemm_bf16(A, B, out=None, out_dtype=None, stream=None):
+    """C = A . B^T (A [M, K], B [N, K], bf16; M <= 16) into ``out`` (fp32 or
+    bf16, may be a strided view).  Returns ``out``."""
+    M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, out_dtype)
+    st = _capi.lib().skinny_gemm_bf16(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,
+                                      lda, ldb, ldc, odt, _stream_handle(stream, A.device))
+    check(st, "skinny_gemm_bf16")
+    return out
+
+
+def skinny_gemm_bf16_with_config(A, B, cfg: SkgConfig, out=None, out_dtype=None, stream=None):
+    """As :func:`skinny_gemm_bf16` with an explicit kernel configuration."""
+    M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, out_dtype)
+    st = _capi.lib().skinny_gemm_bf16_with_config(
+        A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc, odt,
+        _stream_handle(stream, A.device), ctypes.byref(cfg))
+    check(st, "skinny_gemm_bf16_with_config")
+    return out
+
+
+def skinny_gemm_dispatch(M: int, K: int, N: int) -> SkgConfig:
+    cfg = SkgConfig()
+    check(_capi.lib().skinny_gemm_dispatch(M, K, N, ctypes.byref(cfg)), "skinny_gemm_dispatch")
+    return cfg
+
+
+def skinny_gemm_check_config(M: int, K: int, N: int, cfg: SkgConfig) -> bool:
+    return _capi.lib().skinny_gemm_check_config(M, K, N, ctypes.byref(cfg)) == _capi.SKG_OK
+
+
+def skinny_gemm_workspace_bytes(M: int, K: int, N: int, cfg: SkgConfig) -> int:
+    n = ctypes.c_size_t(0)
+    check(_capi.lib().skinny_gemm_workspace_bytes(M, K, N, ctypes.byref(cfg), ctypes.byref(n)),
+          "skinny_gemm_workspace_bytes")
+    return int(n.value)
+
+
+def _pairs(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
+    flat = [v for kn in shapes for v in (int(kn[0]), int(kn[1]))]
+    ms = [int(m) for m in m_values]
+    kn_arr = (ctypes.c_int * max(len(flat), 1))(*flat)
+    m_arr = (ctypes.c_int * max(len(ms), 1))(*ms)
+    return kn_arr, len(flat) // 2, m_arr, len(ms)
+
+
+def skinny_gemm_warmup_keys(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
+    """Distinct dispatch results over (K, N) in ``shapes`` x M in
+    ``m_values``, first-seen order."""
+    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
+    n = ctypes.c_int(0)
+    check(_capi.lib().skinny_gemm_warmup_keys(kn_arr, ns, m_arr, nm, None, 0, ctypes.byref(n)),
+          "skinny_gemm_warmup_keys")
+    buf = (SkgConfig * max(n.value, 1))()
+    check(_capi.lib().skinny_gemm_warmup_keys(kn_arr, ns, m_arr, nm, buf, n.value,
+                                              ctypes.byref(n)), "skinny_gemm_warmup_keys")
+    return [SkgConfig(*buf[i].as_tuple()) for i in range(n.value)]
+
+
+def skinny_gemm_warmup(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int],
+                       stream=None, device=None) -> int:
+    """Loads code, sizes the stream's split-K workspace and runs each distinct
+    configuration once.  Returns the number of distinct configurations."""
+    torch = _torch()
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
+    n = ctypes.c_int(0)
+    with torch.cuda.device(device):
+        check(_capi.lib().skinny_gemm_warmup(kn_arr, ns, m_arr, nm,
+                                             _stream_handle(stream, device), ctypes.byref(n)),
+              "skinny_gemm_warmup")
+    return int(n.value)
+
+
+def skinny_gemm_available() -> bool:
+    return bool(_capi.lib().skinny_gemm_available())
+
+
+def skinny_gemm_strerror(status: int) -> str:
+    return _capi.lib().skinny_gemm_strerror(status).decode()

@@ -1,0 +1,185 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and every host-only function behaves (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latency_decode_gemm_amd as skg
+from latency_decode_gemm_amd import _capi
+from latency_decode_gemm_amd.inputs import all_points
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skinny_gemm.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skinny_gemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    fns = _header_functions()
+    for name in ("skinny_gemm_bf16", "skinny_gemm_dispatch", "skinny_gemm_warmup",
+                 "skinny_gemm_bf16_with_config", "skinny_gemm_warmup_keys"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _capi.lib()
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+        assert name in _capi.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_python_binding_has_same_names():
+    for name in _header_functions():
+        assert callable(getattr(skg, name)), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(_capi.SkgConfig) == 7 * 4
+
+
+def test_strerror_covers_codes():
+    for code in range(7):
+        assert skg.skinny_gemm_strerror(code) != "unknown status"
+    assert skg.skinny_gemm_strerror(99) == "unknown status"
+
+
+def test_dispatch_is_pure_and_deterministic():
+    for p in all_points():
+        first = skg.skinny_gemm_dispatch(p["M"], p["K"], p["N"])
+        assert skg.skinny_gemm_check_config(p["M"], p["K"], p["N"], first)
+        for _ in range(200):
+            assert skg.skinny_gemm_dispatch(p["M"], p["K"], p["N"]) == first
+
+
+def test_dispatch_valid_on_a_shape_grid():
+    for M in range(1, 17):
+        for K in (1, 7, 8, 9, 64, 100, 1000, 1536, 2048, 2880, 4096, 7168, 14336, 20000):
+            for N in (1, 3, 16, 128, 129, 2112, 24576):
+                cfg = skg.skinny_gemm_dispatch(M, K, N)
+                assert skg.skinny_gemm_check_config(M, K, N, cfg), (M, K, N, cfg)
+                assert (cfg.backend == skg.SKG_BACKEND_DOT) == (cfg.split_k == 1)
+
+
+def test_dispatch_rejects():
+    lib = _capi.lib()
+    cfg = _capi.SkgConfig()
+    assert lib.skinny_gemm_dispatch(17, 7168, 256, ctypes.byref(cfg)) == skg.SKG_ERR_UNSUPPORTED
+    assert lib.skinny_gemm_dispatch(0, 7168, 256, ctypes.byref(cfg)) == skg.SKG_ERR_INVALID_ARG
+    assert lib.skinny_gemm_dispatch(1, -1, 256, ctypes.byref(cfg)) == skg.SKG_ERR_INVALID_ARG
+    assert lib.skinny_gemm_dispatch(1, 7168, 256, None) == skg.SKG_ERR_INVALID_ARG
+
+
+def test_check_config_rules():
+    mk = _capi.SkgConfig.make
+    ok = mk(inner=skg.SKG_INNER_VALU, split_k=1, row_tiles=1, waves_n=1, waves_k=4, depth=4)
+    assert skg.skinny_gemm_check_config(4, 7168, 256, ok)
+    bad = [
+        mk(backend=skg.SKG_BACKEND_DOT, split_k=2, row_tiles=1, waves_k=4),     # dot with split
+        mk(backend=skg.SKG_BACKEND_SPLITK, split_k=1, row_tiles=1, waves_k=4),  # split-K of 1
+        mk(row_tiles=3, waves_k=4),                                              # no such variant
+        mk(row_tiles=1, depth=5, waves_k=4),
+        mk(row_tiles=1, waves_n=4, waves_k=4),                                   # 16 waves
+        mk(row_tiles=1, waves_n=0, waves_k=1),
+        mk(split_k=4096, row_tiles=1, waves_k=1),                                # empty splits
+    ]
+    for b in bad:
+        assert not skg.skinny_gemm_check_config(4, 7168, 256, b), b
+    # the staged A slice must fit in 160 KB of LDS: 16 x 7168 x 2 B = 224 KB
+    big = mk(inner=skg.SKG_INNER_MFMA, split_k=1, row_tiles=1, waves_k=4, depth=4)
+    assert not skg.skinny_gemm_check_config(16, 7168, 256, big)
+    assert skg.skinny_gemm_check_config(16, 7168, 256, mk(inner=skg.SKG_INNER_MFMA, split_k=2,
+                                                          row_tiles=1, waves_k=4, depth=4))
+
+
+def test_workspace_bytes():
+    dot = skg.SkgConfig.make(split_k=1, row_tiles=1, waves_k=4)
+    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, dot) == 0
+    sk = skg.SkgConfig.make(split_k=4, row_tiles=1, waves_k=4)
+    rows = 4
+    nrb = 256 // rows
+    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, sk) == nrb * 4 * 4 * rows * 4 + nrb * 4
+
+
+def test_warmup_keys_first_seen_order():
+    shapes = [(7168, 256), (7168, 384), (2880, 128), (1536, 24576)]
+    ms = [1, 2, 3, 4, 8, 16]
+    keys = skg.skinny_gemm_warmup_keys(shapes, ms)
+    want = []
+    for K, N in shapes:
+        for M in ms:
+            c = skg.skinny_gemm_dispatch(M, K, N)
+            if c not in want:
+                want.append(c)
+    assert keys == want
+    assert skg.skinny_gemm_warmup_keys([], ms) == []
+
+
+# --- argument checks run before any HIP call: fake, never-dereferenced pointers
+FAKE = 0x100000  # 16-byte aligned, never touched
+
+
+def _call(A=FAKE, B=FAKE, C=FAKE, M=4, N=256, K=7168, lda=7168, ldb=7168, ldc=256, odt=0):
+    return _capi.lib().skinny_gemm_bf16(A, B, C, M, N, K, lda, ldb, ldc, odt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), skg.SKG_ERR_INVALID_ARG),
+    (dict(N=-1), skg.SKG_ERR_INVALID_ARG),
+    (dict(K=-1), skg.SKG_ERR_INVALID_ARG),
+    (dict(M=17), skg.SKG_ERR_UNSUPPORTED),
+    (dict(odt=2), skg.SKG_ERR_INVALID_ARG),
+    (dict(lda=7160), skg.SKG_ERR_INVALID_ARG),
+    (dict(ldb=100), skg.SKG_ERR_INVALID_ARG),
+    (dict(ldc=255), skg.SKG_ERR_INVALID_ARG),
+    (dict(A=0), skg.SKG_ERR_INVALID_ARG),
+    (dict(B=0), skg.SKG_ERR_INVALID_ARG),
+    (dict(C=0), skg.SKG_ERR_INVALID_ARG),
+    (dict(A=FAKE + 8), skg.SKG_ERR_MISALIGNED),
+    (dict(B=FAKE + 2), skg.SKG_ERR_MISALIGNED),
+    (dict(lda=7172), skg.SKG_ERR_MISALIGNED),
+    (dict(ldb=7176 + 4), skg.SKG_ERR_MISALIGNED),
+    (dict(C=FAKE + 2), skg.SKG_ERR_MISALIGNED),
+    (dict(C=FAKE + 1, odt=1), skg.SKG_ERR_MISALIGNED),
+])
+def test_argument_errors(kw, code):
+    assert _call(**kw) == code
+
+
+def test_empty_problems_are_noops():
+    # nothing to compute: returns before touching the device or the pointers
+    assert _call(M=0) == skg.SKG_OK
+    assert _call(N=0) == skg.SKG_OK
+    assert _call(M=0, A=0, B=0, C=0) == skg.SKG_OK
+
+
+def test_with_config_rejects_bad_config():
+    bad = skg.SkgConfig.make(row_tiles=3)
+    st = _capi.lib().skinny_gemm_bf16_with_config(FAKE, FAKE, FAKE, 4, 256, 7168, 7168, 7168,
+                                                  256, 0, None, ctypes.byref(bad))
+    assert st == skg.SKG_ERR_INVALID_ARG
+    st = _capi.lib().skinny_gemm_bf16_with_config(FAKE, FAKE, FAKE, 4, 256, 7168, 7168, 7168,
+                                                  256, 0, None, None)
+    assert st == skg.SKG_ERR_INVALID_ARG
+
+
+def test_warmup_rejects_bad_lists():
+    lib = _capi.lib()
+    n = ctypes.c_int(0)
+    assert lib.skinny_gemm_warmup(None, 1, None, 0, None, ctypes.byref(n)) == skg.SKG_ERR_INVALID_ARG
+    assert lib.skinny_gemm_warmup(None, -1, None, 0, None, ctypes.byref(n)) == skg.SKG_ERR_INVALID_ARG
+
+
+def test_python_dtype_guard():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((2, 8), dtype=torch.float32)
+    b = torch.zeros((4, 8), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        skg.skinny_gemm_bf16(a, b)
+    with pytest.raises(TypeError):
+        skg.skinny_gemm_bf16(b[:2], a)

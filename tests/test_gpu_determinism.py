@@ -1,0 +1,122 @@
+"""Bit-reproducibility on the GPU: repeated calls, default vs explicit
+configuration, warm-up, concurrent streams, and HIP graph replay."""
+import numpy as np
+import pytest
+
+import latency_decode_gemm_amd as skg
+from latency_decode_gemm_amd import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+MK = skg.SkgConfig.make
+
+
+def _problem(M, K, N):
+    A_bits = inputs.make_a(M, K, N)
+    B_bits = gu.cached_b(K, N)
+    return gu.operands(A_bits, B_bits, K)
+
+
+@pytest.mark.parametrize("shape", [(16, 7168, 256), (4, 7168, 384), (8, 14336, 7168),
+                                   (16, 1536, 24576), (1, 2880, 128)],
+                         ids=lambda s: "M%d_K%d_N%d" % s)
+def test_repeated_calls_identical(shape):
+    torch = gu.torch_cuda()
+    A, B = _problem(*shape)
+    ref = gu.bits_of(skg.skinny_gemm_bf16(A, B))
+    outs = [skg.skinny_gemm_bf16(A, B) for _ in range(50)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(gu.bits_of(o), ref)
+
+
+def test_default_equals_explicit_dispatch_config():
+    torch = gu.torch_cuda()
+    for p in inputs.all_points()[:18]:
+        A, B = _problem(p["M"], p["K"], p["N"])
+        cfg = skg.skinny_gemm_dispatch(p["M"], p["K"], p["N"])
+        c1 = skg.skinny_gemm_bf16(A, B)
+        c2 = skg.skinny_gemm_bf16_with_config(A, B, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits_of(c1), gu.bits_of(c2)), p
+
+
+def test_split_k_forced_is_reproducible():
+    torch = gu.torch_cuda()
+    A, B = _problem(16, 7168, 256)
+    for cfg in (MK(inner=skg.SKG_INNER_MFMA, split_k=8, row_tiles=1, waves_n=1, waves_k=4, depth=4),
+                MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2, depth=4)):
+        ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))
+        for _ in range(100):
+            c = skg.skinny_gemm_bf16_with_config(A, B, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits_of(c), ref)
+
+
+def test_warmup_then_same_bits():
+    torch = gu.torch_cuda()
+    shapes = [(7168, 256), (7168, 384), (2880, 128)]
+    ms = [1, 2, 3, 4, 8, 16]
+    A, B = _problem(16, 7168, 384)
+    before = gu.bits_of(skg.skinny_gemm_bf16(A, B))
+    n = skg.skinny_gemm_warmup(shapes, ms)
+    assert n == len(skg.skinny_gemm_warmup_keys(shapes, ms))
+    assert skg.skinny_gemm_warmup(shapes, ms) == n  # idempotent
+    after = gu.bits_of(skg.skinny_gemm_bf16(A, B))
+    torch.cuda.synchronize()
+    assert np.array_equal(before, after)
+
+
+def test_two_streams_concurrently():
+    torch = gu.torch_cuda()
+    A1, B1 = _problem(16, 7168, 256)
+    A2, B2 = _problem(8, 7168, 384)
+    cfg = MK(inner=skg.SKG_INNER_MFMA, split_k=8, row_tiles=1, waves_n=1, waves_k=4, depth=4)
+    r1 = gu.bits_of(skg.skinny_gemm_bf16_with_config(A1, B1, cfg))
+    r2 = gu.bits_of(skg.skinny_gemm_bf16_with_config(A2, B2, cfg))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs1, outs2 = [], []
+    for _ in range(20):
+        with torch.cuda.stream(s1):
+            outs1.append(skg.skinny_gemm_bf16_with_config(A1, B1, cfg, stream=s1))
+        with torch.cuda.stream(s2):
+            outs2.append(skg.skinny_gemm_bf16_with_config(A2, B2, cfg, stream=s2))
+    torch.cuda.synchronize()
+    for o in outs1:
+        assert np.array_equal(gu.bits_of(o), r1)
+    for o in outs2:
+        assert np.array_equal(gu.bits_of(o), r2)
+
+
+def test_graph_capture_replay():
+    """Captured after warm-up; replayed several times with eager work between;
+    every replay equals the eager result."""
+    torch = gu.torch_cuda()
+    shapes = [(7168, 256), (14336, 7168)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        skg.skinny_gemm_warmup(shapes, [1, 16], stream=s)
+    A1, B1 = _problem(16, 7168, 256)
+    A2, B2 = _problem(1, 14336, 7168)
+    e1 = gu.bits_of(skg.skinny_gemm_bf16(A1, B1))
+    e2 = gu.bits_of(skg.skinny_gemm_bf16(A2, B2, out_dtype=torch.bfloat16))
+    out1 = torch.empty((16, 256), dtype=torch.float32, device="cuda")
+    out2 = torch.empty((1, 7168), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        skg.skinny_gemm_bf16(A1, B1, out=out1, stream=s)
+        skg.skinny_gemm_bf16(A2, B2, out=out2, stream=s)
+    for i in range(4):
+        out1.fill_(float("nan"))
+        out2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits_of(out1), e1), i
+        assert np.array_equal(gu.bits_of(out2), e2), i
+        # eager work between replays
+        skg.skinny_gemm_bf16(A1, B1)
+        torch.cuda.synchronize()

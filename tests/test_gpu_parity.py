@@ -1,0 +1,125 @@
+"""HIP path vs the oracle, element by element (GPU).
+
+* every point of the five decode workloads at full size, with the
+  configuration the dispatch table picks (what bench.py times);
+* every kernel variant forced through the explicit-config entry on shapes
+  that span several row blocks and splits and end in ragged K and N tails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import latency_decode_gemm_amd as skg
+from latency_decode_gemm_amd import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+MK = skg.SkgConfig.make
+V, F = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA
+
+
+def _run_point(p):
+    torch = gu.torch_cuda()
+    M, K, N = p["M"], p["K"], p["N"]
+    A_bits = inputs.make_a(M, K, N)
+    B_bits = gu.cached_b(K, N)
+    A, B = gu.operands(A_bits, B_bits, K)
+    if p["out"] == "bf16":
+        ldc = p["ldc"] or N
+        buf = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+        C = buf[:, :N]
+    else:
+        buf = None
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    skg.skinny_gemm_bf16(A, B, out=C)
+    torch.cuda.synchronize()
+    return A_bits, B_bits, C, buf
+
+
+@pytest.mark.parametrize("p", inputs.all_points(),
+                         ids=lambda p: f"M{p['M']}_K{p['K']}_N{p['N']}_{p['out']}"
+                                       + (f"_ldc{p['ldc']}" if p["ldc"] else ""))
+def test_workload_point(p):
+    A_bits, B_bits, C, buf = _run_point(p)
+    r = gu.assess(C, A_bits, B_bits, p["K"])
+    assert r["ok"], r
+    if buf is not None and buf.shape[1] > p["N"]:
+        # columns [N, ldc) of the strided output are untouched (still NaN)
+        assert np.isnan(gu.to_f64(buf[:, p["N"]:])).all()
+
+
+def _configs():
+    out = []
+    for (R, PF) in [(1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4)]:
+        out += [MK(inner=V, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
+                MK(inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF),
+                MK(inner=V, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF)]
+    for (G, PF) in [(1, 2), (1, 4), (1, 8), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4)]:
+        out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF),
+                MK(inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=3, depth=PF)]
+    return out
+
+
+SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 777, 33),
+          (5, 7168, 100), (11, 520, 50), (2, 9, 5), (13, 33, 300)]
+
+
+def _cfg_id(c):
+    return ("mfma" if c.inner == F else "valu") + f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}" \
+        f"_k{c.waves_k}_d{c.depth}"
+
+
+@pytest.mark.parametrize("cfg", _configs(), ids=_cfg_id)
+def test_forced_config(cfg):
+    torch = gu.torch_cuda()
+    ran = 0
+    for (M, K, N) in SHAPES:
+        ld = gu.round8(K)
+        A_bits = inputs.make_a(M, K, N, lda=ld)
+        B_bits = inputs.make_b(K, N, ldb=ld)
+        A, B = gu.operands(A_bits, B_bits, K)
+        for out_dtype in (torch.float32, torch.bfloat16):
+            if not skg.skinny_gemm_check_config(M, K, N, cfg):
+                with pytest.raises(skg.SkinnyGemmError):
+                    skg.skinny_gemm_bf16_with_config(A, B, cfg, out_dtype=out_dtype)
+                continue
+            C = skg.skinny_gemm_bf16_with_config(A, B, cfg, out_dtype=out_dtype)
+            torch.cuda.synchronize()
+            r = gu.assess(C, A_bits, B_bits, K)
+            assert r["ok"], (M, K, N, out_dtype, r)
+            ran += 1
+    assert ran > 0
+
+
+@pytest.mark.parametrize("variant", [(1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4)],
+                         ids=lambda v: f"r{v[0]}_d{v[1]}")
+def test_every_valu_instantiation(variant):
+    """Each compiled (M, row_tiles, depth) VALU kernel, once."""
+    torch = gu.torch_cuda()
+    R, PF = variant
+    K, N = 1021, 37
+    ld = gu.round8(K)
+    B_bits = inputs.make_b(K, N, ldb=ld)
+    for M in range(1, 17):
+        A_bits = inputs.make_a(M, K, N, lda=ld)
+        A, B = gu.operands(A_bits, B_bits, K)
+        cfg = MK(inner=V, split_k=1, row_tiles=R, waves_n=1, waves_k=2, depth=PF)
+        C = skg.skinny_gemm_bf16_with_config(A, B, cfg)
+        torch.cuda.synchronize()
+        r = gu.assess(C, A_bits, B_bits, K)
+        assert r["ok"], (M, r)
+
+
+def test_default_dispatch_on_small_grid():
+    torch = gu.torch_cuda()
+    for M in (1, 2, 4, 7, 8, 9, 12, 16):
+        for (K, N) in ((64, 16), (300, 45), (2048, 256), (2056, 96)):
+            A_bits = inputs.make_a(M, K, N)
+            B_bits = inputs.make_b(K, N)
+            A, B = gu.operands(A_bits, B_bits, K)
+            C = skg.skinny_gemm_bf16(A, B)
+            torch.cuda.synchronize()
+            r = gu.assess(C, A_bits, B_bits, K)
+            assert r["ok"], (M, K, N, r)
