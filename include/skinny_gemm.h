@@ -64,7 +64,7 @@ typedef enum {
 typedef enum { SKG_OUT_F32 = 0, SKG_OUT_BF16 = 1 } skg_out_dtype;
 
 typedef enum {
-    SKG_BACKEND_DOT = 0,   /* one workgroup per block of rows of B covers all of K */
+    SKG_BACKEND_DOT = 0,   /* each workgroup covers all of K for its blocks of rows of B */
     SKG_BACKEND_SPLITK = 1 /* split_k workgroups per row block, each one slice of K;
                               fp32 partials are summed in a fixed order by the
                               last workgroup to finish (no spin-wait) */
@@ -88,9 +88,11 @@ typedef struct skg_config {
                           MFMA 16*row_tiles (1, 2, 4) */
     int32_t waves_n;   /* waves per workgroup on different rows */
     int32_t waves_k;   /* waves per workgroup on different K slices of the same
-                          rows (combined through LDS); waves_n*waves_k <= 16 */
+                          rows (combined through LDS); waves_n*waves_k <= 8 */
     int32_t depth;     /* K steps of B loads kept in flight per wave
                           (VALU: 2, 4, 8; MFMA: 2, 4, 8; see skinny_gemm_check_config) */
+    int32_t rb_per_wg; /* row blocks (of rows_per_wave*waves_n rows) each workgroup
+                          streams one after another, >= 1; sets the grid size */
 } skg_config;
 
 /*

@@ -41,9 +41,10 @@ class SkgConfig(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("inner", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
                 ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
-                ("depth", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("rb_per_wg", ctypes.c_int32)]
 
-    FIELDS = ("backend", "inner", "split_k", "row_tiles", "waves_n", "waves_k", "depth")
+    FIELDS = ("backend", "inner", "split_k", "row_tiles", "waves_n", "waves_k", "depth",
+              "rb_per_wg")
 
     def as_tuple(self):
         return tuple(getattr(self, f) for f in self.FIELDS)
@@ -53,10 +54,10 @@ class SkgConfig(ctypes.Structure):
 
     @classmethod
     def make(cls, backend=None, inner=SKG_INNER_VALU, split_k=1, row_tiles=1, waves_n=1,
-             waves_k=1, depth=4):
+             waves_k=1, depth=4, rb_per_wg=1):
         if backend is None:
             backend = SKG_BACKEND_DOT if split_k == 1 else SKG_BACKEND_SPLITK
-        return cls(backend, inner, split_k, row_tiles, waves_n, waves_k, depth)
+        return cls(backend, inner, split_k, row_tiles, waves_n, waves_k, depth, rb_per_wg)
 
     def __eq__(self, other):
         return isinstance(other, SkgConfig) and self.as_tuple() == other.as_tuple()

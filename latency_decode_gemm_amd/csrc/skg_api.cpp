@@ -45,29 +45,31 @@ int round_up(int a, int b) { return ceil_div(a, b) * b; }
 bool config_equal(const skg_config &a, const skg_config &b) {
     return a.backend == b.backend && a.inner == b.inner && a.split_k == b.split_k &&
            a.row_tiles == b.row_tiles && a.waves_n == b.waves_n && a.waves_k == b.waves_k &&
-           a.depth == b.depth;
+           a.depth == b.depth && a.rb_per_wg == b.rb_per_wg;
 }
 
 // Default for shapes the table does not list: VALU up to M = 8, MFMA above;
-// enough workgroups to cover the 256 CUs a few times over; A slice <= 64 KB.
+// 4 waves per workgroup (2 on rows x 2 on K); K split only when the staged A
+// slice would exceed 64 KB or the row blocks cannot cover the 256 CUs; each
+// workgroup then streams enough row blocks to keep the grid near 512.
 skg_config default_config(int M, int K, int N) {
     skg_config c;
     std::memset(&c, 0, sizeof c);
     c.inner = (M > 8) ? SKG_INNER_MFMA : SKG_INNER_VALU;
-    c.row_tiles = (c.inner == SKG_INNER_MFMA) ? 1 : (M <= 2 ? 1 : 2);
+    c.row_tiles = (c.inner == SKG_INNER_MFMA) ? 1 : 2;
     c.depth = 4;
-    c.waves_n = 1;
-    c.waves_k = 4;
+    c.waves_n = 2;
+    c.waves_k = 2;
     const int rows_per_wg = (c.inner == SKG_INNER_MFMA ? 16 : 4 * c.row_tiles) * c.waves_n;
     const int num_rb = ceil_div(std::max(N, 1), rows_per_wg);
     const int nck = ceil_div(K, kChunk);
     const int step = (c.inner == SKG_INNER_MFMA) ? kMfmaStep : kValuStep;
     int S = 1;
-    // keep the staged A slice within 64 KB and aim for >= 512 workgroups
     while (S < 16 && (int64_t)M * ceil_div(nck, S) * kChunk * 2 > 64 * 1024) S *= 2;
-    while (S < 16 && num_rb * S < 512 && ceil_div(nck, 2 * S) >= step * c.waves_k) S *= 2;
+    while (S < 16 && num_rb * S < 256 && ceil_div(nck, 2 * S) >= 2 * step * c.waves_k) S *= 2;
     c.split_k = S;
     c.backend = (S > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
+    c.rb_per_wg = std::max(1, (num_rb * S) / 512);
     Geometry g;
     // back off until the geometry is valid (an empty last split, LDS size)
     while (c.split_k > 1 && !make_geometry(M, K, N, c, &g)) {
@@ -181,6 +183,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.num_rb = g.num_rb;
     p.lds_stride = g.lds_stride;
     p.red_offset = g.red_offset;
+    p.flag_offset = g.flag_offset;
     if (cfg.split_k > 1) {
         Workspace w;
         const int st = get_workspace(stream, g.ws_floats, g.n_tickets, &w);
@@ -205,6 +208,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA) return false;
     if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth)) return false;
     if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
+    if (cfg.rb_per_wg < 1) return false;
     Geometry r;
     r.step = (cfg.inner == SKG_INNER_VALU) ? kValuStep : kMfmaStep;
     r.nck = ceil_div(K, kChunk);
@@ -212,6 +216,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.rows_per_wave = (cfg.inner == SKG_INNER_VALU) ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
     r.rows_per_wg = r.rows_per_wave * cfg.waves_n;
     r.num_rb = ceil_div(N, r.rows_per_wg);
+    r.grid_rb = ceil_div(r.num_rb, cfg.rb_per_wg);
     const int S = cfg.split_k;
     const int per_split = ceil_div(std::max(r.nck, 1), S);
     r.wave_chunks = round_up(ceil_div(per_split, cfg.waves_k), r.step);
@@ -220,13 +225,14 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.lds_stride = r.wg_chunks * kChunk + kChunk;
     const size_t a_bytes = (size_t)M * r.lds_stride * 2;
     r.red_offset = (int)((a_bytes + 15) / 16 * 16);
-    const size_t red_bytes = (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
-    r.lds_bytes = r.red_offset + red_bytes + 16;
+    const size_t red_bytes = 2 * (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
+    r.flag_offset = (int)(r.red_offset + red_bytes);
+    r.lds_bytes = r.flag_offset + 16;
     if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
     r.threads = 64 * cfg.waves_n * cfg.waves_k;
     r.ws_floats = (S > 1) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
     r.n_tickets = (S > 1) ? (size_t)r.num_rb : 0;
-    if ((int64_t)r.num_rb * S > 0x7FFFFFFF) return false;
+    if ((int64_t)r.grid_rb * S > 0x7FFFFFFF) return false;
     *g = r;
     return true;
 }

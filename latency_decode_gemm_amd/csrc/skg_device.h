@@ -8,26 +8,35 @@
 // whose partial sums are combined).  The kernels below are designed for CDNA4,
 // not translated from that design:
 //
-//  * One launch streams B exactly once.  A workgroup owns a block of rows of
-//    B (rows_per_wg) and one slice of K; its waves split the rows (waves_n)
-//    and the slice (waves_k).  A[:, slice] is staged once per workgroup in
-//    LDS (zero beyond K) and re-read from LDS; B goes HBM -> VGPRs directly.
+//  * One launch streams B exactly once.  Rows of B are grouped in row blocks
+//    of rows_per_wg rows; K is cut into split_k slices.  A workgroup owns one
+//    K slice and a strided set of row blocks (blockIdx / split_k, then every
+//    gridDim / split_k-th), so it stages A[:, slice] in LDS once (zero beyond
+//    K) and then streams all of its row blocks.  Its waves split the rows of a
+//    block (waves_n) and the slice (waves_k, equal parts).
+//  * Every wave runs one flat stream of K steps over all its row blocks, with
+//    `depth` steps of B loads in flight in a register ring; the loads of the
+//    next row block are already in flight while the current block is reduced
+//    and written.  Barriers inside that stream wait for LDS traffic only, so
+//    they never drain the ring.
 //  * VALU inner product: 16 lanes per row of B, so one 64-lane dwordx4 load
-//    covers 4 rows x 256 contiguous bytes; each lane keeps `depth` K-steps of
-//    loads in flight in a register ring and multiplies with v_dot2c_f32_bf16
-//    (two bf16 products added into fp32).  At the end the 16 lanes of a row
-//    are combined with a DPP reduce-scatter (row_mirror, row_half_mirror,
-//    quad_perm), which leaves lane i of the row group with the sum for m = i.
+//    covers 4 rows x 256 contiguous bytes; products by v_dot2c_f32_bf16 (two
+//    bf16 products added into fp32).  The 16 lanes of a row are combined with
+//    a DPP reduce-scatter (row_mirror, row_half_mirror, quad_perm) that leaves
+//    lane i of the row group with the sum for token m = i.
 //  * MFMA inner product (v_mfma_f32_16x16x32_bf16): the activations are the
 //    16-row operand (rows m >= M are zero), 16 rows of B are the 16 columns;
 //    the instruction performs the K reduction, so no cross-lane step remains.
-//  * Cross-wave (waves_k > 1): partials go through LDS and wave 0 adds them
-//    in wave order.  Cross-workgroup (split_k > 1): each workgroup writes its
-//    fp32 partial tile, releases it at agent scope and takes a ticket; the
-//    workgroup that draws the last ticket acquires, sums the split_k partials
-//    in split order and writes C, then resets the ticket.  Nothing waits for
-//    another workgroup, and the summation order never depends on timing, so
-//    results are bit-reproducible.
+//  * Cross-wave (waves_k > 1): partials go through LDS (double-buffered per
+//    row block) and wave 0 adds them in wave order.  Cross-workgroup
+//    (split_k > 1): each workgroup stores its fp32 partial tile with
+//    agent-scope atomic stores, waits for them, and takes a ticket with one
+//    agent-scope atomic add; the workgroup that draws the last ticket reads the
+//    split_k partials with agent-scope atomic loads, adds them in split order,
+//    writes C and resets the ticket.  These accesses are coherent across the
+//    XCDs' L2s without any L2 write-back or invalidate.  Nothing waits for
+//    another workgroup, and no summation order depends on timing, so results
+//    are bit-reproducible.
 //  * Epilogue: fp32 stores, or bf16 round-to-nearest-even, at C[m*ldc + n];
 //    other bytes of C are never written.
 #pragma once
@@ -51,6 +60,14 @@ __device__ __forceinline__ uint4 lds16(const uint16_t *p) {
 
 __device__ __forceinline__ void sts16(uint16_t *p, uint4 v) {
     *reinterpret_cast<uint4 *>(p) = v;
+}
+
+// Workgroup barrier that orders LDS accesses only: outstanding global loads
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Eight bf16 products accumulated into c, two per v_dot2c_f32_bf16.
@@ -82,27 +99,24 @@ __device__ __forceinline__ void store_c(const KParams &p, int m, int n, float v)
         reinterpret_cast<float *>(p.C)[off] = v;
 }
 
-// One 8-element chunk of row `row` starting at k = 8*c, with everything at
-// k >= K (and every chunk outside [0, c_end)) read as zero.
-__device__ __forceinline__ uint4 load_chunk_masked(const uint16_t *rowp, int c, int c_end,
-                                                   const KParams &p) {
+// One 8-element chunk (k = 8c .. 8c+7) of the row starting at rowp, with
+// every element at k >= K read as zero (no access beyond K).
+__device__ __forceinline__ uint4 load_chunk_masked(const uint16_t *rowp, int c, const KParams &p) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (c < c_end) {
-        if (c < p.nfull) {
-            v = ldg16(rowp + (int64_t)c * kChunk);
-        } else {
-            // the one chunk that straddles K (K % 8 != 0)
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            const int k0 = c * kChunk;
+    if (c < p.nfull) {
+        v = ldg16(rowp + (int64_t)c * kChunk);
+    } else if (c < p.nck) {
+        // the one chunk that straddles K (K % 8 != 0)
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        const int k0 = c * kChunk;
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                if (k0 + e < p.K) {
-                    uint32_t h = rowp[k0 + e];
-                    w[e >> 1] |= h << (16 * (e & 1));
-                }
+        for (int e = 0; e < kChunk; ++e) {
+            if (k0 + e < p.K) {
+                const uint32_t h = rowp[k0 + e];
+                w[e >> 1] |= h << (16 * (e & 1));
             }
-            v = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        v = make_uint4(w[0], w[1], w[2], w[3]);
     }
     return v;
 }
@@ -121,7 +135,7 @@ __device__ __forceinline__ void stage_a(const KParams &p, uint16_t *As, int wg_c
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int m = m0 + i;
-                if (m < MT && m < p.M) v[i] = load_chunk_masked(p.A + (int64_t)m * p.lda, c, p.nck, p);
+                if (m < MT && m < p.M) v[i] = load_chunk_masked(p.A + (int64_t)m * p.lda, c, p);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -205,21 +219,28 @@ struct Pow2Ceil {
     static constexpr int v = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
 };
 
-// ---- split-K completion -----------------------------------------------------
-// Called by every thread of the workgroup after it has stored its partials
-// ws[((rb*S + s)*M + m)*NB + rl].  The workgroup that draws the last ticket
-// adds the S partials of the row block in split order and writes C.
+// ---- split-K ------------------------------------------------------------------
+__device__ __forceinline__ void ws_store(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float ws_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of the workgroup once this workgroup's partials of
+// row block rb are stored (ws_store) and complete (s_waitcnt) in the waves that
+// stored them.  The workgroup that draws the last ticket adds the split_k
+// partials ws[rb][0..S)[m][rl] in split order and writes C.
 __device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsigned *flag) {
-    __threadfence();  // release this thread's partial stores at agent scope
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) {
-        const unsigned t = __hip_atomic_fetch_add(&p.tickets[rb], 1u, __ATOMIC_ACQ_REL,
+        const unsigned t = __hip_atomic_fetch_add(&p.tickets[rb], 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
         *flag = (t == (unsigned)(p.split_k - 1)) ? 1u : 0u;
     }
-    __syncthreads();
+    lds_barrier();
     if (*flag) {
-        __threadfence();  // acquire: the other workgroups' partials are visible
         const int NB = p.rows_per_wg;
         const int total = p.M * NB;
         const float *base = p.ws + (size_t)rb * p.split_k * total;
@@ -229,7 +250,7 @@ __device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsign
             const int row = rb * NB + rl;
             if (row < p.N) {
                 float v = 0.0f;
-                for (int s = 0; s < p.split_k; ++s) v += base[(size_t)s * total + i];
+                for (int s = 0; s < p.split_k; ++s) v += ws_load(base + (size_t)s * total + i);
                 store_c(p, m, row, v);
             }
         }
@@ -238,23 +259,24 @@ __device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsign
     }
 }
 
-// Per-workgroup K range and per-wave K part, in chunks.
-struct KRange {
-    int wg_c0, wv_c0, wv_c1, nsteps, tail_c0;
-    bool has_tail;
+// Work assignment of one workgroup.
+struct WgPlan {
+    int s;       // K slice
+    int rb0;     // first row block
+    int rbs;     // row-block stride
+    int nblk;    // row blocks of this workgroup
+    int wg_c0;   // first chunk of the slice
 };
 
-__device__ __forceinline__ KRange k_range(const KParams &p, int s, int wk, int step) {
-    KRange r;
-    r.wg_c0 = s * p.wg_chunks;
-    const int wg_c1 = min(r.wg_c0 + p.wg_chunks, p.nck);
-    r.wv_c0 = r.wg_c0 + wk * p.wave_chunks;
-    r.wv_c1 = min(r.wv_c0 + p.wave_chunks, wg_c1);
-    const int fc1 = min(r.wv_c1, p.nfull);
-    r.nsteps = fc1 > r.wv_c0 ? (fc1 - r.wv_c0) / step : 0;
-    r.tail_c0 = r.wv_c0 + r.nsteps * step;
-    r.has_tail = r.tail_c0 < r.wv_c1;
-    return r;
+__device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
+    WgPlan w;
+    const int S = p.split_k;
+    w.rb0 = blockIdx.x / S;
+    w.s = blockIdx.x - w.rb0 * S;
+    w.rbs = gridDim.x / S;
+    w.nblk = w.rb0 < p.num_rb ? (p.num_rb - w.rb0 + w.rbs - 1) / w.rbs : 0;
+    w.wg_c0 = w.s * p.wg_chunks;
+    return w;
 }
 
 // ---- VALU kernel --------------------------------------------------------------
@@ -265,8 +287,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *red = reinterpret_cast<float *>(smem + p.red_offset);
-    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.red_offset) +
-                     (p.waves_k - 1) * M * p.rows_per_wg;
+    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -274,28 +295,45 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     const int slot = lane >> 4;
     const int wk = wave / p.waves_n;
     const int wn = wave - wk * p.waves_n;
-    const int rb = blockIdx.x / p.split_k;
-    const int s = blockIdx.x - rb * p.split_k;
-
-    const KRange kr = k_range(p, s, wk, kValuStep);
+    const WgPlan w = wg_plan(p);
+    const int NB = p.rows_per_wg;
+    const int SPB = p.wave_chunks / kValuStep;  // K steps per row block
+    const int T = w.nblk * SPB;
+    const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
     const int rl0 = wn * (4 * R) + slot;  // local row of slot r = 0
-    const int row0 = rb * p.rows_per_wg + rl0;
 
-    const uint16_t *bp[R];
+    // load cursor: row block lb, step lst
+    int lb = 0, lst = 0;
+    const uint16_t *rowp[R];
+    auto set_rows = [&](int b) {
+        const int rbase = (w.rb0 + b * w.rbs) * NB + rl0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = min(row0 + 4 * r, p.N - 1);
-        bp[r] = p.B + (int64_t)row * p.ldb + (int64_t)(kr.wv_c0 + l16) * kChunk;
-    }
+        for (int r = 0; r < R; ++r)
+            rowp[r] = p.B + (int64_t)min(rbase + 4 * r, p.N - 1) * p.ldb;
+    };
+    auto issue = [&](uint4(&dst)[R]) {
+        const int cb = wv_c0 + lst * kValuStep;
+        const int c = cb + l16;
+        if (cb + kValuStep <= p.nfull) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) dst[r] = ldg16(rowp[r] + (int64_t)c * kChunk);
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) dst[r] = load_chunk_masked(rowp[r], c, p);
+        }
+        if (++lst == SPB) {
+            lst = 0;
+            if (++lb < w.nblk) set_rows(lb);
+        }
+    };
 
     uint4 buf[PF][R];
+    if (w.nblk > 0) set_rows(0);
 #pragma unroll
     for (int i = 0; i < PF; ++i)
-        if (i < kr.nsteps)
-#pragma unroll
-            for (int r = 0; r < R; ++r) buf[i][r] = ldg16(bp[r] + i * (kValuStep * kChunk));
+        if (i < T) issue(buf[i]);
 
-    stage_a<M>(p, As, kr.wg_c0);
+    stage_a<M>(p, As, w.wg_c0);
     __syncthreads();
 
     float acc[R][M];
@@ -304,81 +342,81 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-    const uint16_t *ap = As + (kr.wv_c0 - kr.wg_c0 + l16) * kChunk;
-    for (int st = 0; st < kr.nsteps; st += PF) {
+    constexpr int VP = Pow2Ceil<M>::v;
+    const bool writer = l16 < M;
+    const int m_out = l16;
+    const uint16_t *ap = As + (wk * p.wave_chunks + l16) * kChunk;
+    const int red_block = (p.waves_k - 1) * M * NB;  // floats per red buffer
+
+    // epilogue of compute row block b: reduce, combine waves, write
+    auto finish_block = [&](int b) {
+        float res[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float v[VP];
+#pragma unroll
+            for (int j = 0; j < VP; ++j) v[j] = (j < M) ? acc[r][j] : 0.0f;
+            reduce16<VP>(v, lane);
+            res[r] = v[0];
+        }
+        const int rb = w.rb0 + b * w.rbs;
+        if (p.waves_k > 1) {
+            float *rbuf = red + (b & 1) * red_block;
+            if (wk > 0 && writer)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    rbuf[((wk - 1) * M + m_out) * NB + rl0 + 4 * r] = res[r];
+            lds_barrier();
+            if (wk == 0 && writer)
+                for (int q = 1; q < p.waves_k; ++q)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        res[r] += rbuf[((q - 1) * M + m_out) * NB + rl0 + 4 * r];
+        }
+        const int row0 = rb * NB + rl0;
+        if (p.split_k == 1) {
+            if (wk == 0 && writer)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (row0 + 4 * r < p.N) store_c(p, m_out, row0 + 4 * r, res[r]);
+        } else {
+            if (wk == 0) {
+                if (writer) {
+                    float *dst = p.ws + ((size_t)(rb * p.split_k + w.s) * M + m_out) * NB;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) ws_store(dst + rl0 + 4 * r, res[r]);
+                }
+                __builtin_amdgcn_s_waitcnt(0);  // partial stores complete
+            }
+            splitk_complete(p, rb, flag);
+        }
+    };
+
+    int cb = 0, cst = 0;  // compute cursor
+    for (int t0 = 0; t0 < T; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (st + i < kr.nsteps) {
+            if (t0 + i < T) {
+                const uint16_t *a_st = ap + cst * (kValuStep * kChunk);
                 uint4 a[M];
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    a[m] = lds16(ap + m * p.lds_stride + (st + i) * (kValuStep * kChunk));
+                for (int m = 0; m < M; ++m) a[m] = lds16(a_st + m * p.lds_stride);
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int m = 0; m < M; ++m) acc[r][m] = dot8(a[m], buf[i][r], acc[r][m]);
-                if (st + i + PF < kr.nsteps)
+                if (t0 + i + PF < T) issue(buf[i]);
+                if (++cst == SPB) {
+                    finish_block(cb);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        buf[i][r] = ldg16(bp[r] + (st + i + PF) * (kValuStep * kChunk));
+#pragma unroll
+                        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+                    cst = 0;
+                    ++cb;
+                }
             }
         }
-    }
-    if (kr.has_tail) {
-        const int c = kr.tail_c0 + l16;
-        uint4 b[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = min(row0 + 4 * r, p.N - 1);
-            b[r] = load_chunk_masked(p.B + (int64_t)row * p.ldb, c, kr.wv_c1, p);
-        }
-        const uint16_t *apt = As + (c - kr.wg_c0) * kChunk;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint4 a = lds16(apt + m * p.lds_stride);
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][m] = dot8(a, b[r], acc[r][m]);
-        }
-    }
-
-    // 16 lanes of a row -> lane l16 holds the sum for m = l16 (if l16 < M)
-    constexpr int VP = Pow2Ceil<M>::v;
-    float res[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float v[VP];
-#pragma unroll
-        for (int j = 0; j < VP; ++j) v[j] = (j < M) ? acc[r][j] : 0.0f;
-        reduce16<VP>(v, lane);
-        res[r] = v[0];
-    }
-    const bool writer = l16 < M;
-    const int m = l16;
-    const int NB = p.rows_per_wg;
-
-    if (p.waves_k > 1) {
-        if (wk > 0 && writer)
-#pragma unroll
-            for (int r = 0; r < R; ++r) red[((wk - 1) * M + m) * NB + rl0 + 4 * r] = res[r];
-        __syncthreads();
-        if (wk == 0 && writer)
-            for (int w = 1; w < p.waves_k; ++w)
-#pragma unroll
-                for (int r = 0; r < R; ++r) res[r] += red[((w - 1) * M + m) * NB + rl0 + 4 * r];
-    }
-
-    if (p.split_k == 1) {
-        if (wk == 0 && writer)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (row0 + 4 * r < p.N) store_c(p, m, row0 + 4 * r, res[r]);
-    } else {
-        if (wk == 0 && writer) {
-            float *dst = p.ws + ((size_t)(rb * p.split_k + s) * M + m) * NB;
-#pragma unroll
-            for (int r = 0; r < R; ++r) dst[rl0 + 4 * r] = res[r];
-        }
-        splitk_complete(p, rb, flag);
     }
 }
 
@@ -390,8 +428,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *red = reinterpret_cast<float *>(smem + p.red_offset);
-    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.red_offset) +
-                     (p.waves_k - 1) * p.M * p.rows_per_wg;
+    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -399,28 +436,45 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     const int g4 = lane >> 4;  // which 8-element chunk of the 32-wide K step
     const int wk = wave / p.waves_n;
     const int wn = wave - wk * p.waves_n;
-    const int rb = blockIdx.x / p.split_k;
-    const int s = blockIdx.x - rb * p.split_k;
+    const WgPlan w = wg_plan(p);
+    const int NB = p.rows_per_wg;
+    const int M = p.M;
+    const int SPB = p.wave_chunks / kMfmaStep;
+    const int T = w.nblk * SPB;
+    const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
+    const int rlw = wn * (16 * G);  // first local row of this wave
 
-    const KRange kr = k_range(p, s, wk, kMfmaStep);
-    const int rlw = wn * (16 * G);           // first local row of this wave
-    const int rowb = rb * p.rows_per_wg + rlw;  // first global row of this wave
-
-    const uint16_t *bp[G];
+    int lb = 0, lst = 0;
+    const uint16_t *rowp[G];
+    auto set_rows = [&](int b) {
+        const int rbase = (w.rb0 + b * w.rbs) * NB + rlw + j;
 #pragma unroll
-    for (int t = 0; t < G; ++t) {
-        const int row = min(rowb + 16 * t + j, p.N - 1);
-        bp[t] = p.B + (int64_t)row * p.ldb + (int64_t)(kr.wv_c0 + g4) * kChunk;
-    }
+        for (int t = 0; t < G; ++t)
+            rowp[t] = p.B + (int64_t)min(rbase + 16 * t, p.N - 1) * p.ldb;
+    };
+    auto issue = [&](uint4(&dst)[G]) {
+        const int cb = wv_c0 + lst * kMfmaStep;
+        const int c = cb + g4;
+        if (cb + kMfmaStep <= p.nfull) {
+#pragma unroll
+            for (int t = 0; t < G; ++t) dst[t] = ldg16(rowp[t] + (int64_t)c * kChunk);
+        } else {
+#pragma unroll
+            for (int t = 0; t < G; ++t) dst[t] = load_chunk_masked(rowp[t], c, p);
+        }
+        if (++lst == SPB) {
+            lst = 0;
+            if (++lb < w.nblk) set_rows(lb);
+        }
+    };
 
     uint4 buf[PF][G];
+    if (w.nblk > 0) set_rows(0);
 #pragma unroll
     for (int i = 0; i < PF; ++i)
-        if (i < kr.nsteps)
-#pragma unroll
-            for (int t = 0; t < G; ++t) buf[i][t] = ldg16(bp[t] + i * (kMfmaStep * kChunk));
+        if (i < T) issue(buf[i]);
 
-    stage_a<16>(p, As, kr.wg_c0);
+    stage_a<16>(p, As, w.wg_c0);
     __syncthreads();
 
     f32x4_t acc[G];
@@ -428,89 +482,87 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // rows m >= M of the activation operand are zero: read a valid row and mask
-    const uint32_t amask = (j < p.M) ? 0xFFFFFFFFu : 0u;
-    const int jm = min(j, p.M - 1);
-    const uint16_t *ap = As + jm * p.lds_stride + (kr.wv_c0 - kr.wg_c0 + g4) * kChunk;
+    const uint32_t amask = (j < M) ? 0xFFFFFFFFu : 0u;
+    const uint16_t *ap = As + min(j, M - 1) * p.lds_stride + (wk * p.wave_chunks + g4) * kChunk;
+    const int red_block = (p.waves_k - 1) * M * NB;
 
-    for (int st = 0; st < kr.nsteps; st += PF) {
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            if (st + i < kr.nsteps) {
-                uint4 a = lds16(ap + (st + i) * (kMfmaStep * kChunk));
-                a.x &= amask; a.y &= amask; a.z &= amask; a.w &= amask;
-                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-                for (int t = 0; t < G; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        av, __builtin_bit_cast(bf16x8_t, buf[i][t]), acc[t], 0, 0, 0);
-                if (st + i + PF < kr.nsteps)
-#pragma unroll
-                    for (int t = 0; t < G; ++t)
-                        buf[i][t] = ldg16(bp[t] + (st + i + PF) * (kMfmaStep * kChunk));
-            }
-        }
-    }
-    if (kr.has_tail) {
-        const int c = kr.tail_c0 + g4;
-        uint4 a = lds16(As + jm * p.lds_stride + (c - kr.wg_c0) * kChunk);
-        a.x &= amask; a.y &= amask; a.z &= amask; a.w &= amask;
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-        for (int t = 0; t < G; ++t) {
-            const int row = min(rowb + 16 * t + j, p.N - 1);
-            const uint4 b = load_chunk_masked(p.B + (int64_t)row * p.ldb, c, kr.wv_c1, p);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, b),
-                                                             acc[t], 0, 0, 0);
-        }
-    }
-
-    // acc[t][v] holds C[m = 4*g4 + v][row = rowb + 16*t + j]
-    const int NB = p.rows_per_wg;
-    const int M = p.M;
-    if (p.waves_k > 1) {
-        if (wk > 0)
-#pragma unroll
-            for (int t = 0; t < G; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 4 * g4 + v;
-                    if (m < M) red[((wk - 1) * M + m) * NB + rlw + 16 * t + j] = acc[t][v];
-                }
-        __syncthreads();
-        if (wk == 0)
-            for (int w = 1; w < p.waves_k; ++w)
+    // acc[t][v] holds C[m = 4*g4 + v][row = row block base + rlw + 16*t + j]
+    auto finish_block = [&](int b) {
+        const int rb = w.rb0 + b * w.rbs;
+        if (p.waves_k > 1) {
+            float *rbuf = red + (b & 1) * red_block;
+            if (wk > 0)
 #pragma unroll
                 for (int t = 0; t < G; ++t)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int m = 4 * g4 + v;
-                        if (m < M) acc[t][v] += red[((w - 1) * M + m) * NB + rlw + 16 * t + j];
+                        if (m < M) rbuf[((wk - 1) * M + m) * NB + rlw + 16 * t + j] = acc[t][v];
                     }
-    }
+            lds_barrier();
+            if (wk == 0)
+                for (int q = 1; q < p.waves_k; ++q)
+#pragma unroll
+                    for (int t = 0; t < G; ++t)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int m = 4 * g4 + v;
+                            if (m < M) acc[t][v] += rbuf[((q - 1) * M + m) * NB + rlw + 16 * t + j];
+                        }
+        }
+        const int rowb = rb * NB + rlw + j;
+        if (p.split_k == 1) {
+            if (wk == 0)
+#pragma unroll
+                for (int t = 0; t < G; ++t) {
+                    const int row = rowb + 16 * t;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = 4 * g4 + v;
+                        if (m < M && row < p.N) store_c(p, m, row, acc[t][v]);
+                    }
+                }
+        } else {
+            if (wk == 0) {
+                float *dst = p.ws + (size_t)(rb * p.split_k + w.s) * M * NB;
+#pragma unroll
+                for (int t = 0; t < G; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = 4 * g4 + v;
+                        if (m < M) ws_store(dst + m * NB + rlw + 16 * t + j, acc[t][v]);
+                    }
+                __builtin_amdgcn_s_waitcnt(0);  // partial stores complete
+            }
+            splitk_complete(p, rb, flag);
+        }
+    };
 
-    if (p.split_k == 1) {
-        if (wk == 0)
+    int cb = 0, cst = 0;
+    for (int t0 = 0; t0 < T; t0 += PF) {
 #pragma unroll
-            for (int t = 0; t < G; ++t) {
-                const int row = rowb + 16 * t + j;
+        for (int i = 0; i < PF; ++i) {
+            if (t0 + i < T) {
+                uint4 a = lds16(ap + cst * (kMfmaStep * kChunk));
+                a.x &= amask;
+                a.y &= amask;
+                a.z &= amask;
+                a.w &= amask;
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 4 * g4 + v;
-                    if (m < M && row < p.N) store_c(p, m, row, acc[t][v]);
+                for (int t = 0; t < G; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        av, __builtin_bit_cast(bf16x8_t, buf[i][t]), acc[t], 0, 0, 0);
+                if (t0 + i + PF < T) issue(buf[i]);
+                if (++cst == SPB) {
+                    finish_block(cb);
+#pragma unroll
+                    for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    cst = 0;
+                    ++cb;
                 }
             }
-    } else {
-        if (wk == 0) {
-            float *dst = p.ws + (size_t)(rb * p.split_k + s) * M * NB;
-#pragma unroll
-            for (int t = 0; t < G; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 4 * g4 + v;
-                    if (m < M) dst[m * NB + rlw + 16 * t + j] = acc[t][v];
-                }
         }
-        splitk_complete(p, rb, flag);
     }
 }
 

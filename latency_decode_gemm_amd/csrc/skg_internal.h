@@ -40,6 +40,8 @@ struct KParams {
     int num_rb;
     int lds_stride;   // bf16 elements per staged A row in LDS
     int red_offset;   // byte offset of the cross-wave reduction area in LDS
+                      // (two buffers of (waves_k-1)*M*rows_per_wg floats)
+    int flag_offset;  // byte offset of the split-K "last arrival" flag in LDS
 };
 
 // Derived launch geometry for (M, K, N, cfg).
@@ -48,10 +50,11 @@ struct Geometry {
     int nck, nfull;
     int wave_chunks, wg_chunks;
     int rows_per_wave, rows_per_wg, num_rb;
+    int grid_rb;       // workgroups per K slice (each takes every grid_rb-th row block)
     int threads;
     int lds_stride;    // elements
     size_t lds_bytes;
-    int red_offset;
+    int red_offset, flag_offset;
     size_t ws_floats;  // split-K partial floats
     size_t n_tickets;
 };

@@ -1,6 +1,8 @@
 // skg_launch.hip -- MFMA kernel instantiations, the zero-fill kernel, and
 // the launch path shared by every variant.
 #include <algorithm>
+#include <mutex>
+#include <set>
 
 #include "skg_device.h"
 
@@ -56,7 +58,20 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
                   hipStream_t stream) {
     KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth);
     if (!fn) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)g.num_rb * (unsigned)cfg.split_k;
+    if (g.lds_bytes > 64 * 1024) {
+        // allow this kernel the full LDS of a CU (once per kernel)
+        static std::mutex mu;
+        static std::set<KernelPtr> done;
+        std::lock_guard<std::mutex> lock(mu);
+        if (!done.count(fn)) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxLdsBytes);
+            if (e != hipSuccess) return e;
+            done.insert(fn);
+        }
+    }
+    const unsigned grid = (unsigned)g.grid_rb * (unsigned)cfg.split_k;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(g.threads), g.lds_bytes, stream, p);
     return hipGetLastError();
 }

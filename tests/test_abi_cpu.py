@@ -40,7 +40,7 @@ def test_python_binding_has_same_names():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(_capi.SkgConfig) == 7 * 4
+    assert ctypes.sizeof(_capi.SkgConfig) == 8 * 4
 
 
 def test_strerror_covers_codes():

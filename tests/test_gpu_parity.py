@@ -116,8 +116,9 @@ def test_default_dispatch_on_small_grid():
     torch = gu.torch_cuda()
     for M in (1, 2, 4, 7, 8, 9, 12, 16):
         for (K, N) in ((64, 16), (300, 45), (2048, 256), (2056, 96)):
-            A_bits = inputs.make_a(M, K, N)
-            B_bits = inputs.make_b(K, N)
+            ld = gu.round8(K)
+            A_bits = inputs.make_a(M, K, N, lda=ld)
+            B_bits = inputs.make_b(K, N, ldb=ld)
             A, B = gu.operands(A_bits, B_bits, K)
             C = skg.skinny_gemm_bf16(A, B)
             torch.cuda.synchronize()
