@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default=None,
                     help="profile helper: run only the point 'M,K,N' (no JSON checks)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB once "
+                         "(a plain copy kernel of known size, for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -298,6 +301,15 @@ def main():
     if bad:
         print(f"bench.py: results do not match the oracle: {bad}", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_probe_mb:
+        nbytes = args.copy_probe_mb << 20
+        src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     traffic = load_traffic(dom.name())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,

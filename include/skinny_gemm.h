@@ -71,8 +71,13 @@ typedef enum {
 } skg_backend;
 
 typedef enum {
-    SKG_INNER_VALU = 0, /* bf16 dot2 instructions, 16 lanes per row of B */
-    SKG_INNER_MFMA = 1  /* 16x16x32 bf16 matrix-core tiles (M padded to 16) */
+    SKG_INNER_VALU = 0,    /* bf16 dot2 instructions, 16 lanes per row of B;
+                              A staged in LDS */
+    SKG_INNER_MFMA = 1,    /* 16x16x32 bf16 matrix-core tiles (M padded to 16);
+                              A staged in LDS */
+    SKG_INNER_MFMA_GA = 2  /* as SKG_INNER_MFMA, with the activation fragments
+                              read from global memory (L2) each K step: no LDS
+                              for A, so any K fits in one workgroup */
 } skg_inner;
 
 #define SKG_MAX_M 16
@@ -85,12 +90,14 @@ typedef struct skg_config {
     int32_t inner;     /* skg_inner */
     int32_t split_k;   /* workgroups along K per row block */
     int32_t row_tiles; /* rows per wave: VALU 4*row_tiles (1, 2, 4);
-                          MFMA 16*row_tiles (1, 2, 4) */
+                          MFMA and MFMA_GA 16*row_tiles (1, 2, 4) */
     int32_t waves_n;   /* waves per workgroup on different rows */
     int32_t waves_k;   /* waves per workgroup on different K slices of the same
                           rows (combined through LDS); waves_n*waves_k <= 8 */
-    int32_t depth;     /* K steps of B loads kept in flight per wave
-                          (VALU: 2, 4, 8; MFMA: 2, 4, 8; see skinny_gemm_check_config) */
+    int32_t depth;     /* 128-wide K steps of loads kept in flight per wave.
+                          Compiled (row_tiles, depth) pairs: VALU (1,4) (1,8) (2,2)
+                          (2,4) (4,2) (4,4); MFMA and MFMA_GA (1,2) (1,3) (1,4)
+                          (2,1) (2,2) (4,1) */
     int32_t rb_per_wg; /* row blocks (of rows_per_wave*waves_n rows) each workgroup
                           streams one after another, >= 1; sets the grid size */
 } skg_config;

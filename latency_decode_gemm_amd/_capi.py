@@ -27,7 +27,12 @@ SKG_BACKEND_DOT = 0
 SKG_BACKEND_SPLITK = 1
 SKG_INNER_VALU = 0
 SKG_INNER_MFMA = 1
+SKG_INNER_MFMA_GA = 2
 SKG_MAX_M = 16
+
+# Compiled (row_tiles, depth) pairs per inner product (the library's tables).
+VALU_VARIANTS = ((1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4))
+MFMA_VARIANTS = ((1, 2), (1, 3), (1, 4), (2, 1), (2, 2), (4, 1))
 
 # Every function the header declares, with (restype, argtypes).
 _i = ctypes.c_int

@@ -55,17 +55,19 @@ bool config_equal(const skg_config &a, const skg_config &b) {
 skg_config default_config(int M, int K, int N) {
     skg_config c;
     std::memset(&c, 0, sizeof c);
-    c.inner = (M > 8) ? SKG_INNER_MFMA : SKG_INNER_VALU;
-    c.row_tiles = (c.inner == SKG_INNER_MFMA) ? 1 : 2;
+    c.inner = (M > 8) ? SKG_INNER_MFMA_GA : SKG_INNER_VALU;
+    c.row_tiles = (c.inner == SKG_INNER_VALU) ? 2 : 1;
     c.depth = 4;
     c.waves_n = 2;
     c.waves_k = 2;
-    const int rows_per_wg = (c.inner == SKG_INNER_MFMA ? 16 : 4 * c.row_tiles) * c.waves_n;
+    const int rows_per_wg = (c.inner == SKG_INNER_VALU ? 4 * c.row_tiles : 16) * c.waves_n;
     const int num_rb = ceil_div(std::max(N, 1), rows_per_wg);
     const int nck = ceil_div(K, kChunk);
-    const int step = (c.inner == SKG_INNER_MFMA) ? kMfmaStep : kValuStep;
+    const int step = kValuStep;
     int S = 1;
-    while (S < 16 && (int64_t)M * ceil_div(nck, S) * kChunk * 2 > 64 * 1024) S *= 2;
+    while (c.inner == SKG_INNER_VALU && S < 16 &&
+           (int64_t)M * ceil_div(nck, S) * kChunk * 2 > 64 * 1024)
+        S *= 2;
     while (S < 16 && num_rb * S < 256 && ceil_div(nck, 2 * S) >= 2 * step * c.waves_k) S *= 2;
     c.split_k = S;
     c.backend = (S > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
@@ -184,6 +186,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.lds_stride = g.lds_stride;
     p.red_offset = g.red_offset;
     p.flag_offset = g.flag_offset;
+    p.tr_offset = g.tr_offset;
     if (cfg.split_k > 1) {
         Workspace w;
         const int st = get_workspace(stream, g.ws_floats, g.n_tickets, &w);
@@ -205,12 +208,14 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     } else {
         return false;
     }
-    if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA) return false;
+    if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA &&
+        cfg.inner != SKG_INNER_MFMA_GA)
+        return false;
     if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth)) return false;
     if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
     if (cfg.rb_per_wg < 1) return false;
     Geometry r;
-    r.step = (cfg.inner == SKG_INNER_VALU) ? kValuStep : kMfmaStep;
+    r.step = kValuStep;
     r.nck = ceil_div(K, kChunk);
     r.nfull = K / kChunk;
     r.rows_per_wave = (cfg.inner == SKG_INNER_VALU) ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
@@ -222,9 +227,19 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.wave_chunks = round_up(ceil_div(per_split, cfg.waves_k), r.step);
     r.wg_chunks = r.wave_chunks * cfg.waves_k;
     if ((int64_t)(S - 1) * r.wg_chunks >= std::max(r.nck, 1)) return false;  // empty split
+    // staged activations: VALU rows of lds_stride elements (padded by one
+    // chunk); MFMA one 1 KB operand fragment per 32-wide K step; MFMA_GA none
     r.lds_stride = r.wg_chunks * kChunk + kChunk;
-    const size_t a_bytes = (size_t)M * r.lds_stride * 2;
-    r.red_offset = (int)((a_bytes + 15) / 16 * 16);
+    size_t a_bytes = 0;
+    if (cfg.inner == SKG_INNER_VALU)
+        a_bytes = (size_t)M * r.lds_stride * 2;
+    else if (cfg.inner == SKG_INNER_MFMA)
+        a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16;
+    r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
+    const size_t tr_bytes = (cfg.inner == SKG_INNER_VALU)
+                                ? 0
+                                : (size_t)cfg.waves_n * cfg.waves_k * cfg.row_tiles * kTileBytes;
+    r.red_offset = (int)(r.tr_offset + tr_bytes);
     const size_t red_bytes = 2 * (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
     r.flag_offset = (int)(r.red_offset + red_bytes);
     r.lds_bytes = r.flag_offset + 16;

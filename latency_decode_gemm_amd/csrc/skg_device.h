@@ -49,9 +49,17 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
     return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Weight loads: every byte of B is read once, so they are marked
+// non-temporal (streaming) and do not displace A from the caches.
+__device__ __forceinline__ uint4 ldg16_stream(const uint16_t *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ uint4 lds16(const uint16_t *p) {
@@ -101,10 +109,11 @@ __device__ __forceinline__ void store_c(const KParams &p, int m, int n, float v)
 
 // One 8-element chunk (k = 8c .. 8c+7) of the row starting at rowp, with
 // every element at k >= K read as zero (no access beyond K).
+template <bool STREAM = false>
 __device__ __forceinline__ uint4 load_chunk_masked(const uint16_t *rowp, int c, const KParams &p) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (c < p.nfull) {
-        v = ldg16(rowp + (int64_t)c * kChunk);
+        v = STREAM ? ldg16_stream(rowp + (int64_t)c * kChunk) : ldg16(rowp + (int64_t)c * kChunk);
     } else if (c < p.nck) {
         // the one chunk that straddles K (K % 8 != 0)
         uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -316,10 +325,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         const int c = cb + l16;
         if (cb + kValuStep <= p.nfull) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) dst[r] = ldg16(rowp[r] + (int64_t)c * kChunk);
+            for (int r = 0; r < R; ++r) dst[r] = ldg16_stream(rowp[r] + (int64_t)c * kChunk);
         } else {
 #pragma unroll
-            for (int r = 0; r < R; ++r) dst[r] = load_chunk_masked(rowp[r], c, p);
+            for (int r = 0; r < R; ++r) dst[r] = load_chunk_masked<true>(rowp[r], c, p);
         }
         if (++lst == SPB) {
             lst = 0;
@@ -421,9 +430,45 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 }
 
 // ---- MFMA kernel ------------------------------------------------------------
-// G: 16-row tiles per wave; PF: K-steps of B loads in flight.  M <= 16 at run
-// time (activation rows m >= M are fed as zeros).
-template <int G, int PF>
+// Stage A[:, slice] in LDS in MFMA operand order: for each 32-wide K step, the
+// 64 lane fragments (lane l: token m = l & 15, chunk l >> 4 of the step) lie
+// contiguously, so the per-step operand read is one conflict-free 1 KB
+// ds_read_b128.  Tokens m >= M are stored as zeros.
+__device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int wg_c0) {
+    const int nch = p.wg_chunks;
+    for (int cc = threadIdx.x; cc < nch; cc += blockDim.x) {
+        const int c = wg_c0 + cc;
+        uint16_t *dst = As + ((cc >> 2) * 64 + 16 * (cc & 3)) * kChunk;
+#pragma unroll
+        for (int m0 = 0; m0 < 16; m0 += 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int m = m0 + i;
+                v[i] = make_uint4(0u, 0u, 0u, 0u);
+                if (m < p.M) v[i] = load_chunk_masked(p.A + (int64_t)m * p.lda, c, p);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sts16(dst + (m0 + i) * kChunk, v[i]);
+        }
+    }
+}
+
+// The MFMA B operand wants lane l to hold 8 consecutive k of row (l & 15);
+// loading it that way makes every quarter-wave touch 16 rows (16 B each),
+// which streams far slower than one 256-byte row segment per quarter-wave.
+// So B is loaded with the VALU layout (lane l: row 4q + (l >> 4), chunk
+// l & 15, q = 0..3 over four loads = 16 rows x 128 k) and transposed through
+// a wave-private 4 KB LDS tile: (row r, chunk c) sits in 16-byte slot
+// r * 16 + (c ^ r), so the writes (one row per quarter-wave) and the operand
+// reads (16 rows, one chunk each per quarter-wave) both hit 16 distinct slots.
+__device__ __forceinline__ int tile_slot(int r, int c) { return r * 16 + (c ^ r); }
+
+// G: 16-row tiles per wave; PF: 128-wide K steps of loads in flight; AG: the
+// activation fragments of each step are loaded from global memory (L2-
+// resident, in the same register ring as B) instead of being staged in LDS.
+// M <= 16 at run time (activation rows m >= M are fed as zeros).
+template <int G, int PF, bool AG>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
@@ -432,35 +477,53 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int j = lane & 15;   // operand row: token m for A, row of B for B
-    const int g4 = lane >> 4;  // which 8-element chunk of the 32-wide K step
+    const int lo = lane & 15;  // load: chunk within the step; operand: row / token
+    const int hi = lane >> 4;  // load: row within a group of 4; operand: chunk of 4
     const int wk = wave / p.waves_n;
     const int wn = wave - wk * p.waves_n;
     const WgPlan w = wg_plan(p);
     const int NB = p.rows_per_wg;
     const int M = p.M;
-    const int SPB = p.wave_chunks / kMfmaStep;
+    const int SPB = p.wave_chunks / kValuStep;
     const int T = w.nblk * SPB;
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
     const int rlw = wn * (16 * G);  // first local row of this wave
+    uint4 *tile = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (G * 256);
+    // activation row of this lane (AG): rows m >= M read row M-1 and are masked
+    const uint16_t *arow = p.A + (int64_t)min(lo, M - 1) * p.lda;
+    const uint32_t amask = (lo < M) ? 0xFFFFFFFFu : 0u;
 
     int lb = 0, lst = 0;
-    const uint16_t *rowp[G];
+    const uint16_t *rowp[G][4];
     auto set_rows = [&](int b) {
-        const int rbase = (w.rb0 + b * w.rbs) * NB + rlw + j;
+        const int rbase = (w.rb0 + b * w.rbs) * NB + rlw + hi;
 #pragma unroll
         for (int t = 0; t < G; ++t)
-            rowp[t] = p.B + (int64_t)min(rbase + 16 * t, p.N - 1) * p.ldb;
-    };
-    auto issue = [&](uint4(&dst)[G]) {
-        const int cb = wv_c0 + lst * kMfmaStep;
-        const int c = cb + g4;
-        if (cb + kMfmaStep <= p.nfull) {
 #pragma unroll
-            for (int t = 0; t < G; ++t) dst[t] = ldg16(rowp[t] + (int64_t)c * kChunk);
+            for (int q = 0; q < 4; ++q)
+                rowp[t][q] = p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb;
+    };
+    auto issue = [&](uint4(&dst)[G][4], uint4(&adst)[4]) {
+        const int cb = wv_c0 + lst * kValuStep;
+        const int c = cb + lo;
+        if (cb + kValuStep <= p.nfull) {
+#pragma unroll
+            for (int t = 0; t < G; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dst[t][q] = ldg16_stream(rowp[t][q] + (int64_t)c * kChunk);
+            if constexpr (AG)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    adst[s] = ldg16(arow + (int64_t)(cb + 4 * s + hi) * kChunk);
         } else {
 #pragma unroll
-            for (int t = 0; t < G; ++t) dst[t] = load_chunk_masked(rowp[t], c, p);
+            for (int t = 0; t < G; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[t][q] = load_chunk_masked<true>(rowp[t][q], c, p);
+            if constexpr (AG)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) adst[s] = load_chunk_masked(arow, cb + 4 * s + hi, p);
         }
         if (++lst == SPB) {
             lst = 0;
@@ -468,25 +531,27 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
         }
     };
 
-    uint4 buf[PF][G];
+    uint4 buf[PF][G][4];
+    uint4 abuf[PF][4];
     if (w.nblk > 0) set_rows(0);
 #pragma unroll
     for (int i = 0; i < PF; ++i)
-        if (i < T) issue(buf[i]);
+        if (i < T) issue(buf[i], abuf[i]);
 
-    stage_a<16>(p, As, w.wg_c0);
-    __syncthreads();
+    if constexpr (!AG) {
+        stage_a_frag(p, As, w.wg_c0);
+        __syncthreads();
+    }
 
     f32x4_t acc[G];
 #pragma unroll
     for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // rows m >= M of the activation operand are zero: read a valid row and mask
-    const uint32_t amask = (j < M) ? 0xFFFFFFFFu : 0u;
-    const uint16_t *ap = As + min(j, M - 1) * p.lds_stride + (wk * p.wave_chunks + g4) * kChunk;
+    // LDS activation fragments of this wave: one 1 KB block per 32-wide step
+    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
     const int red_block = (p.waves_k - 1) * M * NB;
 
-    // acc[t][v] holds C[m = 4*g4 + v][row = row block base + rlw + 16*t + j]
+    // acc[t][v] holds C[m = 4*hi + v][row = row block base + rlw + 16*t + lo]
     auto finish_block = [&](int b) {
         const int rb = w.rb0 + b * w.rbs;
         if (p.waves_k > 1) {
@@ -496,8 +561,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                 for (int t = 0; t < G; ++t)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * g4 + v;
-                        if (m < M) rbuf[((wk - 1) * M + m) * NB + rlw + 16 * t + j] = acc[t][v];
+                        const int m = 4 * hi + v;
+                        if (m < M) rbuf[((wk - 1) * M + m) * NB + rlw + 16 * t + lo] = acc[t][v];
                     }
             lds_barrier();
             if (wk == 0)
@@ -506,11 +571,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                     for (int t = 0; t < G; ++t)
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const int m = 4 * g4 + v;
-                            if (m < M) acc[t][v] += rbuf[((q - 1) * M + m) * NB + rlw + 16 * t + j];
+                            const int m = 4 * hi + v;
+                            if (m < M) acc[t][v] += rbuf[((q - 1) * M + m) * NB + rlw + 16 * t + lo];
                         }
         }
-        const int rowb = rb * NB + rlw + j;
+        const int rowb = rb * NB + rlw + lo;
         if (p.split_k == 1) {
             if (wk == 0)
 #pragma unroll
@@ -518,7 +583,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                     const int row = rowb + 16 * t;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * g4 + v;
+                        const int m = 4 * hi + v;
                         if (m < M && row < p.N) store_c(p, m, row, acc[t][v]);
                     }
                 }
@@ -529,8 +594,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                 for (int t = 0; t < G; ++t)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * g4 + v;
-                        if (m < M) ws_store(dst + m * NB + rlw + 16 * t + j, acc[t][v]);
+                        const int m = 4 * hi + v;
+                        if (m < M) ws_store(dst + m * NB + rlw + 16 * t + lo, acc[t][v]);
                     }
                 __builtin_amdgcn_s_waitcnt(0);  // partial stores complete
             }
@@ -543,17 +608,32 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             if (t0 + i < T) {
-                uint4 a = lds16(ap + cst * (kMfmaStep * kChunk));
-                a.x &= amask;
-                a.y &= amask;
-                a.z &= amask;
-                a.w &= amask;
-                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+                // transpose this step's B (16 rows x 16 chunks per tile) through LDS
 #pragma unroll
                 for (int t = 0; t < G; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        av, __builtin_bit_cast(bf16x8_t, buf[i][t]), acc[t], 0, 0, 0);
-                if (t0 + i + PF < T) issue(buf[i]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) tile[t * 256 + tile_slot(4 * q + hi, lo)] = buf[i][t][q];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    uint4 a;
+                    if constexpr (AG) {
+                        a = abuf[i][s];
+                        a.x &= amask;
+                        a.y &= amask;
+                        a.z &= amask;
+                        a.w &= amask;
+                    } else {
+                        a = lds16(ap + (cst * 4 + s) * (64 * kChunk));
+                    }
+                    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+                    for (int t = 0; t < G; ++t) {
+                        const uint4 bv = tile[t * 256 + tile_slot(lo, 4 * s + hi)];
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av, __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
+                    }
+                }
+                if (t0 + i + PF < T) issue(buf[i], abuf[i]);
                 if (++cst == SPB) {
                     finish_block(cb);
 #pragma unroll

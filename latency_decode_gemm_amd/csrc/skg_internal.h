@@ -12,10 +12,9 @@ namespace skg {
 
 // K is walked in chunks of 8 bf16 (one 16-byte load).
 constexpr int kChunk = 8;
-// K-step of one wave, in chunks: VALU = 16 lanes x 1 chunk, MFMA = 4 lane
-// groups x 1 chunk (32 k per 16x16x32 instruction).
+// K-step of one wave, in chunks (both kernels): 16 lanes x 1 chunk = 128 k;
+// the MFMA kernel runs four 16x16x32 instructions per step.
 constexpr int kValuStep = 16;
-constexpr int kMfmaStep = 4;
 // gfx950 LDS per workgroup.
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
@@ -42,6 +41,7 @@ struct KParams {
     int red_offset;   // byte offset of the cross-wave reduction area in LDS
                       // (two buffers of (waves_k-1)*M*rows_per_wg floats)
     int flag_offset;  // byte offset of the split-K "last arrival" flag in LDS
+    int tr_offset;    // byte offset of the MFMA kernel's per-wave transpose tiles
 };
 
 // Derived launch geometry for (M, K, N, cfg).
@@ -54,7 +54,7 @@ struct Geometry {
     int threads;
     int lds_stride;    // elements
     size_t lds_bytes;
-    int red_offset, flag_offset;
+    int red_offset, flag_offset, tr_offset;
     size_t ws_floats;  // split-K partial floats
     size_t n_tickets;
 };
@@ -75,6 +75,9 @@ hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
 
 // Loads a kernel's code object (forces lazy loading) for availability checks.
 hipError_t probe_kernels();
+
+// MFMA transpose tile per wave and 16-row tile: 16 rows x 16 chunks x 16 B.
+constexpr int kTileBytes = 4096;
 
 // Kernel variants.  VALU (row_tiles R, depth PF) pairs, in table order; the
 // instantiations live in skg_valu_lo.hip (M = 1..8) and skg_valu_hi.hip

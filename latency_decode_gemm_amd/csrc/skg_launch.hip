@@ -25,12 +25,13 @@ __global__ void skg_zero_fill_kernel(void *C, int M, int N, int64_t ldc, int out
 
 struct MfmaVariant {
     int G, PF;
-    KernelPtr fn;
+    KernelPtr lds_a;     // activations staged in LDS
+    KernelPtr global_a;  // activation fragments loaded from global memory
 };
-const MfmaVariant kMfmaVariants[] = {
-    {1, 2, skg_mfma_kernel<1, 2>}, {1, 4, skg_mfma_kernel<1, 4>}, {1, 8, skg_mfma_kernel<1, 8>},
-    {2, 2, skg_mfma_kernel<2, 2>}, {2, 4, skg_mfma_kernel<2, 4>}, {2, 8, skg_mfma_kernel<2, 8>},
-    {4, 2, skg_mfma_kernel<4, 2>}, {4, 4, skg_mfma_kernel<4, 4>}};
+#define SKG_MFMA(G, PF) {G, PF, skg_mfma_kernel<G, PF, false>, skg_mfma_kernel<G, PF, true>}
+const MfmaVariant kMfmaVariants[] = {SKG_MFMA(1, 2), SKG_MFMA(1, 3), SKG_MFMA(1, 4),
+                                     SKG_MFMA(2, 1), SKG_MFMA(2, 2), SKG_MFMA(4, 1)};
+#undef SKG_MFMA
 constexpr int kNumMfma = sizeof(kMfmaVariants) / sizeof(kMfmaVariants[0]);
 
 KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
@@ -40,10 +41,11 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
                 return M <= 8 ? valu_kernel_lo(M, i) : valu_kernel_hi(M, i);
         return nullptr;
     }
-    if (inner == SKG_INNER_MFMA) {
+    if (inner == SKG_INNER_MFMA || inner == SKG_INNER_MFMA_GA) {
         for (int i = 0; i < kNumMfma; ++i)
             if (kMfmaVariants[i].G == row_tiles && kMfmaVariants[i].PF == depth)
-                return kMfmaVariants[i].fn;
+                return inner == SKG_INNER_MFMA ? kMfmaVariants[i].lds_a
+                                               : kMfmaVariants[i].global_a;
     }
     return nullptr;
 }

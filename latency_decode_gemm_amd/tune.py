@@ -25,21 +25,20 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
 
-VALU_VARIANTS = [(1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4)]
-MFMA_VARIANTS = [(1, 2), (1, 4), (1, 8), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4)]
+from latency_decode_gemm_amd._capi import MFMA_VARIANTS, VALU_VARIANTS
 WAVES = [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2), (1, 4), (2, 4), (1, 8)]
 SPLITS = [1, 2, 3, 4, 6, 8, 12, 16]
 GRID_TARGETS = [256, 512, 1024, 2048]
 
 
 def rows_per_wave(inner, rt):
-    return 4 * rt if inner == 0 else 16 * rt
+    return 4 * rt if inner == 0 else 16 * rt  # inner 1, 2: MFMA tiles of 16 rows
 
 
 def structures(skg, M, K, N, inner_set):
     """(inner, rt, depth, wn, wk, S, rb_per_wg) tuples for stage 1."""
     out = []
-    mid_depth = {0: {1: 8, 2: 4, 4: 2}, 1: {1: 4, 2: 4, 4: 2}}
+    mid_depth = {0: {1: 8, 2: 4, 4: 2}, 1: {1: 3, 2: 2, 4: 1}, 2: {1: 3, 2: 2, 4: 1}}
     for inner in inner_set:
         for rt in (1, 2, 4):
             d = mid_depth[inner][rt]
@@ -210,7 +209,7 @@ def main():
             odt = skg.SKG_OUT_BF16 if out == "bf16" else skg.SKG_OUT_F32
             C = torch.zeros((M, ldc), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                             device="cuda")
-            inner_set = [0, 1] if 2 <= M <= 12 else ([0] if M < 2 else [1, 0])
+            inner_set = [0, 1, 2] if 2 <= M <= 12 else ([0] if M < 2 else [1, 2, 0])
             cands = structures(skg, M, K, N, inner_set)
             timed = {}
             for cfg in cands:

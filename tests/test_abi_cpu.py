@@ -97,6 +97,17 @@ def test_check_config_rules():
                                                           row_tiles=1, waves_k=4, depth=4))
 
 
+def test_compiled_variant_lists_match_library():
+    for inner, allowed in ((skg.SKG_INNER_VALU, _capi.VALU_VARIANTS),
+                           (skg.SKG_INNER_MFMA, _capi.MFMA_VARIANTS),
+                           (skg.SKG_INNER_MFMA_GA, _capi.MFMA_VARIANTS)):
+        for rt in (1, 2, 3, 4, 8):
+            for d in range(0, 10):
+                cfg = skg.SkgConfig.make(inner=inner, row_tiles=rt, depth=d, waves_k=2)
+                ok = skg.skinny_gemm_check_config(4, 1024, 512, cfg)
+                assert ok == ((rt, d) in allowed), (inner, rt, d)
+
+
 def test_workspace_bytes():
     dot = skg.SkgConfig.make(split_k=1, row_tiles=1, waves_k=4)
     assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, dot) == 0

@@ -45,7 +45,7 @@ def test_default_equals_explicit_dispatch_config():
 def test_split_k_forced_is_reproducible():
     torch = gu.torch_cuda()
     A, B = _problem(16, 7168, 256)
-    for cfg in (MK(inner=skg.SKG_INNER_MFMA, split_k=8, row_tiles=1, waves_n=1, waves_k=4, depth=4),
+    for cfg in (MK(inner=skg.SKG_INNER_MFMA, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=2),
                 MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2, depth=4)):
         ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))
         for _ in range(100):
@@ -72,7 +72,7 @@ def test_two_streams_concurrently():
     torch = gu.torch_cuda()
     A1, B1 = _problem(16, 7168, 256)
     A2, B2 = _problem(8, 7168, 384)
-    cfg = MK(inner=skg.SKG_INNER_MFMA, split_k=8, row_tiles=1, waves_n=1, waves_k=4, depth=4)
+    cfg = MK(inner=skg.SKG_INNER_MFMA, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=2)
     r1 = gu.bits_of(skg.skinny_gemm_bf16_with_config(A1, B1, cfg))
     r2 = gu.bits_of(skg.skinny_gemm_bf16_with_config(A2, B2, cfg))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()

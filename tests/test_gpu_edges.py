@@ -27,7 +27,9 @@ def _sentinel(M, ldc, bf16):
 CFGS = [None,
         MK(inner=V, split_k=2, row_tiles=1, waves_n=1, waves_k=2, depth=4),
         MK(inner=F, split_k=1, row_tiles=1, waves_n=1, waves_k=2, depth=4),
-        MK(inner=F, split_k=3, row_tiles=1, waves_n=2, waves_k=1, depth=2)]
+        MK(inner=F, split_k=3, row_tiles=1, waves_n=2, waves_k=1, depth=2),
+        MK(inner=skg.SKG_INNER_MFMA_GA, split_k=1, row_tiles=2, waves_n=1, waves_k=3, depth=2,
+           rb_per_wg=2)]
 
 
 def _call(A, B, cfg, out):

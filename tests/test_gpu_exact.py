@@ -15,7 +15,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 MK = skg.SkgConfig.make
-V, F = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA
+V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 
 FAMILIES = [
     None,  # the dispatch table's choice
@@ -24,14 +24,17 @@ FAMILIES = [
     MK(inner=V, split_k=3, row_tiles=4, waves_n=1, waves_k=2, depth=2),
     MK(inner=F, split_k=1, row_tiles=1, waves_n=1, waves_k=1, depth=4),
     MK(inner=F, split_k=1, row_tiles=2, waves_n=2, waves_k=4, depth=2),
-    MK(inner=F, split_k=4, row_tiles=4, waves_n=1, waves_k=2, depth=4),
+    MK(inner=F, split_k=4, row_tiles=4, waves_n=1, waves_k=2, depth=1),
+    MK(inner=GA, split_k=1, row_tiles=1, waves_n=1, waves_k=4, depth=3, rb_per_wg=2),
+    MK(inner=GA, split_k=2, row_tiles=2, waves_n=2, waves_k=1, depth=1),
 ]
 
 
 def _fid(c):
     if c is None:
         return "dispatch"
-    return ("mfma" if c.inner == F else "valu") + f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}"
+    return {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
+        f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
 
 
 def _gemm(A, B, cfg, out_dtype):

@@ -16,7 +16,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 MK = skg.SkgConfig.make
-V, F = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA
+V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 
 
 def _run_point(p):
@@ -51,14 +51,17 @@ def test_workload_point(p):
 
 def _configs():
     out = []
-    for (R, PF) in [(1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4)]:
+    for (R, PF) in skg._capi.VALU_VARIANTS:
         out += [MK(inner=V, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
-                MK(inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF),
-                MK(inner=V, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF)]
-    for (G, PF) in [(1, 2), (1, 4), (1, 8), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4)]:
+                MK(inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF, rb_per_wg=3),
+                MK(inner=V, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2)]
+    for (G, PF) in skg._capi.MFMA_VARIANTS:
         out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 MK(inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF),
-                MK(inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=3, depth=PF)]
+                MK(inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=3, depth=PF, rb_per_wg=2),
+                MK(inner=GA, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(inner=GA, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF, rb_per_wg=3),
+                MK(inner=GA, split_k=3, row_tiles=G, waves_n=1, waves_k=2, depth=PF)]
     return out
 
 
@@ -67,8 +70,8 @@ SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 7
 
 
 def _cfg_id(c):
-    return ("mfma" if c.inner == F else "valu") + f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}" \
-        f"_k{c.waves_k}_d{c.depth}"
+    return {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
+        f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_d{c.depth}_b{c.rb_per_wg}"
 
 
 @pytest.mark.parametrize("cfg", _configs(), ids=_cfg_id)
@@ -93,7 +96,7 @@ def test_forced_config(cfg):
     assert ran > 0
 
 
-@pytest.mark.parametrize("variant", [(1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4)],
+@pytest.mark.parametrize("variant", list(skg._capi.VALU_VARIANTS),
                          ids=lambda v: f"r{v[0]}_d{v[1]}")
 def test_every_valu_instantiation(variant):
     """Each compiled (M, row_tiles, depth) VALU kernel, once."""
