@@ -117,6 +117,16 @@ int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
                      int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
                      void *stream);
 
+/* Same as skinny_gemm_bf16, and the dispatch of the (single) kernel records
+ * start_event when the kernel starts and stop_event when it ends (hipEvent_t
+ * handles passed as void*, either may be NULL; created by the caller with
+ * timing enabled).  hipEventElapsedTime(start, stop) is then the kernel's own
+ * duration, without the launch gap a stream-recorded event pair includes.
+ * Nothing is recorded when the call returns early (M == 0 or N == 0, errors). */
+int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, int K,
+                           int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
+                           void *stream, void *start_event, void *stop_event);
+
 /* Same as skinny_gemm_bf16 with an explicit configuration (tests, tuning).
  * An invalid or unsupported configuration returns SKG_ERR_INVALID_ARG. */
 int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M,

@@ -7,9 +7,10 @@ tensors into that ABI.  ``inputs`` holds the seeded synthetic-input recipe.
 from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_SPLITK, SKG_ERR_HIP, SKG_ERR_INVALID_ARG,
                     SKG_ERR_MISALIGNED, SKG_ERR_NO_DEVICE, SKG_ERR_NOT_WARMED,
                     SKG_ERR_UNSUPPORTED, SKG_INNER_MFMA, SKG_INNER_MFMA_GA, SKG_INNER_VALU, SKG_MAX_M, SKG_OK,
-                    SKG_OUT_BF16, SKG_OUT_F32, SkgConfig, SkinnyGemmError)
-from .ops import (skinny_gemm_available, skinny_gemm_bf16, skinny_gemm_bf16_with_config,
+                    SKG_OUT_BF16, SKG_OUT_F32, HipEvent, SkgConfig, SkinnyGemmError)
+from .ops import (skinny_gemm_available, skinny_gemm_bf16, skinny_gemm_bf16_timed,
+                  skinny_gemm_bf16_with_config,
                   skinny_gemm_check_config, skinny_gemm_dispatch, skinny_gemm_strerror,
                   skinny_gemm_warmup, skinny_gemm_warmup_keys, skinny_gemm_workspace_bytes)
 
-__all__ = [n for n in dir() if n.startswith(("skinny_gemm", "SKG_", "Skg", "Skinny"))]
+__all__ = [n for n in dir() if n.startswith(("skinny_gemm", "SKG_", "Skg", "Skinny", "Hip"))]

@@ -78,6 +78,8 @@ _cfgp = ctypes.POINTER(SkgConfig)
 
 SIGNATURES = {
     "skinny_gemm_bf16": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp]),
+    "skinny_gemm_bf16_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp,
+                                    _vp, _vp]),
     "skinny_gemm_bf16_with_config": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i,
                                           _vp, _cfgp]),
     "skinny_gemm_dispatch": (_i, [_i, _i, _i, _cfgp]),
@@ -110,6 +112,40 @@ def lib() -> ctypes.CDLL:
                     fn.argtypes = args
                 _lib = dll
     return _lib
+
+
+class HipEvent:
+    """A timing hipEvent_t (for skinny_gemm_bf16_timed), via the HIP runtime."""
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if self._rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if self._rt().hipEventSynchronize(end.handle) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self._rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and self.handle:
+            self._hip.hipEventDestroy(self.handle)
 
 
 class SkinnyGemmError(RuntimeError):

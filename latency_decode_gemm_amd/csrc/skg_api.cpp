@@ -153,10 +153,14 @@ int check_args(const void *A, const void *B, const void *C, int M, int N, int K,
 }
 
 int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda, int64_t ldb,
-        int64_t ldc, int out_dtype, void *stream_v, const skg_config &cfg) {
+        int64_t ldc, int out_dtype, void *stream_v, const skg_config &cfg,
+        void *start_v = nullptr, void *stop_v = nullptr) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    hipEvent_t start = reinterpret_cast<hipEvent_t>(start_v);
+    hipEvent_t stop = reinterpret_cast<hipEvent_t>(stop_v);
     if (K == 0) {
-        return launch_zero_fill(C, M, N, ldc, out_dtype == SKG_OUT_BF16, stream) == hipSuccess
+        return launch_zero_fill(C, M, N, ldc, out_dtype == SKG_OUT_BF16, stream, start, stop) ==
+                       hipSuccess
                    ? SKG_OK
                    : SKG_ERR_HIP;
     }
@@ -194,7 +198,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
         p.ws = w.ws;
         p.tickets = w.tickets;
     }
-    return launch(p, g, cfg, stream) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
+    return launch(p, g, cfg, stream, start, stop) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
 }
 
 }  // namespace
@@ -298,6 +302,17 @@ int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
     const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
     if (ds != SKG_OK) return ds;
     return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg);
+}
+
+int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, int K,
+                           int64_t lda, int64_t ldb, int64_t ldc, int out_dtype, void *stream,
+                           void *start_event, void *stop_event) {
+    const int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, out_dtype);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    skg_config cfg;
+    const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
+    if (ds != SKG_OK) return ds;
+    return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg, start_event, stop_event);
 }
 
 int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M, int N, int K,

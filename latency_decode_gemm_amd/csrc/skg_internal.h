@@ -65,13 +65,15 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g);
 // Whether (inner, row_tiles, depth) has a compiled kernel.
 bool variant_exists(int inner, int row_tiles, int depth);
 
-// Enqueues the kernel(s) for p with geometry g on stream.
+// Enqueues the kernel for p with geometry g on stream.  Non-null start/stop
+// events are recorded by the dispatch itself (kernel start and end).
 hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
-                  hipStream_t stream);
+                  hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Zero-fills C[m*ldc + n] for K == 0.
 hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
-                            hipStream_t stream);
+                            hipStream_t stream, hipEvent_t start = nullptr,
+                            hipEvent_t stop = nullptr);
 
 // Loads a kernel's code object (forces lazy loading) for availability checks.
 hipError_t probe_kernels();

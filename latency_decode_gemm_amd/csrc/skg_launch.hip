@@ -57,7 +57,7 @@ bool variant_exists(int inner, int row_tiles, int depth) {
 }
 
 hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
-                  hipStream_t stream) {
+                  hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth);
     if (!fn) return hipErrorInvalidValue;
     if (g.lds_bytes > 64 * 1024) {
@@ -74,14 +74,25 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
         }
     }
     const unsigned grid = (unsigned)g.grid_rb * (unsigned)cfg.split_k;
+    if (start || stop) {
+        KParams arg = p;
+        void *args[] = {&arg};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(g.threads),
+                                  args, g.lds_bytes, stream, start, stop, 0);
+    }
     hipLaunchKernelGGL(fn, dim3(grid), dim3(g.threads), g.lds_bytes, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const int64_t total = (int64_t)M * N;
     const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+    if (start || stop) {
+        void *args[] = {&C, &M, &N, &ldc, &out_bf16};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(skg_zero_fill_kernel),
+                                  dim3(blocks), dim3(256), args, 0, stream, start, stop, 0);
+    }
     hipLaunchKernelGGL(skg_zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, C, M, N, ldc,
                        out_bf16);
     return hipGetLastError();

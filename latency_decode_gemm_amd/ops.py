@@ -78,6 +78,20 @@ def skinny_gemm_bf16(A, B, out=None, out_dtype=None, stream=None):
     return out
 
 
+def skinny_gemm_bf16_timed(A, B, start_event, stop_event, out=None, out_dtype=None, stream=None):
+    """As :func:`skinny_gemm_bf16`; the kernel's own start and end are
+    recorded in ``start_event`` / ``stop_event`` (:class:`HipEvent` or raw
+    hipEvent_t handles)."""
+    M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, out_dtype)
+    h0 = getattr(start_event, "handle", start_event)
+    h1 = getattr(stop_event, "handle", stop_event)
+    st = _capi.lib().skinny_gemm_bf16_timed(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,
+                                            lda, ldb, ldc, odt, _stream_handle(stream, A.device),
+                                            h0, h1)
+    check(st, "skinny_gemm_bf16_timed")
+    return out
+
+
 def skinny_gemm_bf16_with_config(A, B, cfg: SkgConfig, out=None, out_dtype=None, stream=None):
     """As :func:`skinny_gemm_bf16` with an explicit kernel configuration."""
     M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, out_dtype)

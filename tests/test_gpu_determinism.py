@@ -120,3 +120,26 @@ def test_graph_capture_replay():
         # eager work between replays
         skg.skinny_gemm_bf16(A1, B1)
         torch.cuda.synchronize()
+
+
+def test_timed_entry_records_kernel_duration():
+    """skinny_gemm_bf16_timed gives the same bits as skinny_gemm_bf16 and its
+    events bracket the kernel itself (positive, and no longer than a pair of
+    stream events recorded around the same call)."""
+    torch = gu.torch_cuda()
+    A, B = _problem(16, 14336, 7168)
+    ref = gu.bits_of(skg.skinny_gemm_bf16(A, B, out_dtype=torch.bfloat16))
+    e0, e1 = skg.HipEvent(), skg.HipEvent()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    durs, outer = [], []
+    for _ in range(5):
+        s0.record()
+        out = skg.skinny_gemm_bf16_timed(A, B, e0, e1, out_dtype=torch.bfloat16)
+        s1.record()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits_of(out), ref)
+        durs.append(e0.elapsed_ms(e1))
+        outer.append(s0.elapsed_time(s1))
+    assert min(durs) > 0.0
+    assert np.median(durs) <= np.median(outer) * 1.02
