@@ -240,9 +240,11 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     else if (cfg.inner == SKG_INNER_MFMA)
         a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
-    const size_t tr_bytes = (cfg.inner == SKG_INNER_VALU)
-                                ? 0
-                                : (size_t)cfg.waves_n * cfg.waves_k * cfg.row_tiles * kTileBytes;
+    // MFMA: one transpose tile per 16-row tile of B per wave, plus one for A (GA)
+    const int tiles = (cfg.inner == SKG_INNER_VALU)  ? 0
+                      : (cfg.inner == SKG_INNER_MFMA) ? cfg.row_tiles
+                                                      : cfg.row_tiles + 1;
+    const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
     r.red_offset = (int)(r.tr_offset + tr_bytes);
     const size_t red_bytes = 2 * (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
     r.flag_offset = (int)(r.red_offset + red_bytes);

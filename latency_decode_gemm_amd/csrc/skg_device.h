@@ -70,6 +70,16 @@ __device__ __forceinline__ void sts16(uint16_t *p, uint4 v) {
     *reinterpret_cast<uint4 *>(p) = v;
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes from gsrc land at lds_base + 16 * l (lds_base is the same
+// for the whole wave).  No VGPRs are used, so every staging load of a
+// workgroup can be in flight at once; the data is in LDS once vmcnt drains.
+__device__ __forceinline__ void lds_dma16(const uint16_t *gsrc, void *lds_base) {
+    typedef const __attribute__((address_space(1))) void *gptr_t;
+    typedef __attribute__((address_space(3))) void *lptr_t;
+    __builtin_amdgcn_global_load_lds((gptr_t)(gsrc), (lptr_t)(lds_base), 16, 0, 0);
+}
+
 // Workgroup barrier that orders LDS accesses only: outstanding global loads
 // stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -131,26 +141,27 @@ __device__ __forceinline__ uint4 load_chunk_masked(const uint16_t *rowp, int c, 
 }
 
 // Stage A[m, 8*wg_c0 : 8*(wg_c0 + wg_chunks)) for m < M into LDS rows of
-// p.lds_stride elements; zeros beyond K.  Up to 8 rows' loads are issued
-// before their LDS stores so the latencies overlap.
-template <int MT>  // MT: compile-time upper bound of M
+// p.lds_stride elements; zeros beyond K.  Each wave moves blocks of 64 chunks
+// (1 KB, one row) straight into LDS; the chunk straddling K and the chunks
+// beyond it are written as (partial) zeros by ordinary LDS stores.  The
+// caller's barrier waits for all of it.
 __device__ __forceinline__ void stage_a(const KParams &p, uint16_t *As, int wg_c0) {
+    const int lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
     const int nch = p.wg_chunks;
-    for (int cc = threadIdx.x; cc < nch; cc += blockDim.x) {
+    const int nblk = (nch + 63) >> 6;  // 64-chunk blocks per row
+    for (int blk = threadIdx.x >> 6; blk < p.M * nblk; blk += nwaves) {
+        const int m = blk / nblk;
+        const int cc0 = (blk - m * nblk) << 6;
+        const int cc = cc0 + lane;
         const int c = wg_c0 + cc;
-#pragma unroll
-        for (int m0 = 0; m0 < MT; m0 += 8) {
-            uint4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int m = m0 + i;
-                if (m < MT && m < p.M) v[i] = load_chunk_masked(p.A + (int64_t)m * p.lda, c, p);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int m = m0 + i;
-                if (m < MT && m < p.M) sts16(As + m * p.lds_stride + cc * kChunk, v[i]);
-            }
+        const uint16_t *rowp = p.A + (int64_t)m * p.lda;
+        uint16_t *dst = As + m * p.lds_stride + cc0 * kChunk;
+        if (cc < nch) {
+            if (c < p.nfull)
+                lds_dma16(rowp + (int64_t)c * kChunk, dst);
+            else
+                sts16(dst + lane * kChunk, load_chunk_masked(rowp, c, p));
         }
     }
 }
@@ -342,7 +353,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     for (int i = 0; i < PF; ++i)
         if (i < T) issue(buf[i]);
 
-    stage_a<M>(p, As, w.wg_c0);
+    stage_a(p, As, w.wg_c0);
     __syncthreads();
 
     float acc[R][M];
@@ -433,24 +444,22 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 // Stage A[:, slice] in LDS in MFMA operand order: for each 32-wide K step, the
 // 64 lane fragments (lane l: token m = l & 15, chunk l >> 4 of the step) lie
 // contiguously, so the per-step operand read is one conflict-free 1 KB
-// ds_read_b128.  Tokens m >= M are stored as zeros.
+// ds_read_b128.  One direct-to-LDS load per step block; tokens m >= M load
+// row M-1 (the readers mask them to zero); chunks at or beyond K are written
+// as (partial) zeros by ordinary LDS stores.
 __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int wg_c0) {
-    const int nch = p.wg_chunks;
-    for (int cc = threadIdx.x; cc < nch; cc += blockDim.x) {
-        const int c = wg_c0 + cc;
-        uint16_t *dst = As + ((cc >> 2) * 64 + 16 * (cc & 3)) * kChunk;
-#pragma unroll
-        for (int m0 = 0; m0 < 16; m0 += 8) {
-            uint4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int m = m0 + i;
-                v[i] = make_uint4(0u, 0u, 0u, 0u);
-                if (m < p.M) v[i] = load_chunk_masked(p.A + (int64_t)m * p.lda, c, p);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sts16(dst + (m0 + i) * kChunk, v[i]);
-        }
+    const int lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int m = min(lane & 15, p.M - 1);
+    const uint16_t *rowp = p.A + (int64_t)m * p.lda;
+    const int nblk = p.wg_chunks >> 2;  // 32-wide steps
+    for (int blk = threadIdx.x >> 6; blk < nblk; blk += nwaves) {
+        const int c = wg_c0 + 4 * blk + (lane >> 4);
+        uint16_t *dst = As + blk * 64 * kChunk;
+        if (c < p.nfull)
+            lds_dma16(rowp + (int64_t)c * kChunk, dst);
+        else
+            sts16(dst + lane * kChunk, load_chunk_masked(rowp, c, p));
     }
 }
 
@@ -465,8 +474,9 @@ __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int
 __device__ __forceinline__ int tile_slot(int r, int c) { return r * 16 + (c ^ r); }
 
 // G: 16-row tiles per wave; PF: 128-wide K steps of loads in flight; AG: the
-// activation fragments of each step are loaded from global memory (L2-
-// resident, in the same register ring as B) instead of being staged in LDS.
+// activations of each step are loaded from global memory (L2-resident, in the
+// same register ring as B, with the same row-segment layout) and transposed
+// through their own wave-private tile, instead of being staged in LDS.
 // M <= 16 at run time (activation rows m >= M are fed as zeros).
 template <int G, int PF, bool AG>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
@@ -488,10 +498,17 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     const int T = w.nblk * SPB;
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
     const int rlw = wn * (16 * G);  // first local row of this wave
-    uint4 *tile = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (G * 256);
-    // activation row of this lane (AG): rows m >= M read row M-1 and are masked
-    const uint16_t *arow = p.A + (int64_t)min(lo, M - 1) * p.lda;
-    const uint32_t amask = (lo < M) ? 0xFFFFFFFFu : 0u;
+    constexpr int NT = G + (AG ? 1 : 0);  // transpose tiles per wave (B tiles, then A)
+    uint4 *tile = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (NT * 256);
+    // AG: activation rows 4q + hi of this lane (rows >= M read row M-1, masked)
+    const int aq = (M + 3) >> 2;  // activation loads per step
+    const uint16_t *arow[4];
+    uint32_t amask[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        arow[q] = p.A + (int64_t)min(4 * q + hi, M - 1) * p.lda;
+        amask[q] = (4 * q + hi < M) ? 0xFFFFFFFFu : 0u;
+    }
 
     int lb = 0, lst = 0;
     const uint16_t *rowp[G][4];
@@ -514,8 +531,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                     dst[t][q] = ldg16_stream(rowp[t][q] + (int64_t)c * kChunk);
             if constexpr (AG)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    adst[s] = ldg16(arow + (int64_t)(cb + 4 * s + hi) * kChunk);
+                for (int q = 0; q < 4; ++q)
+                    if (q < aq) adst[q] = ldg16(arow[q] + (int64_t)c * kChunk);
         } else {
 #pragma unroll
             for (int t = 0; t < G; ++t)
@@ -523,7 +540,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                 for (int q = 0; q < 4; ++q) dst[t][q] = load_chunk_masked<true>(rowp[t][q], c, p);
             if constexpr (AG)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) adst[s] = load_chunk_masked(arow, cb + 4 * s + hi, p);
+                for (int q = 0; q < 4; ++q)
+                    if (q < aq) adst[q] = load_chunk_masked(arow[q], c, p);
         }
         if (++lst == SPB) {
             lst = 0;
@@ -547,8 +565,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // LDS activation fragments of this wave: one 1 KB block per 32-wide step
+    // LDS activation fragments of this wave: one 1 KB block per 32-wide step;
+    // lanes of tokens m >= M zero what they read
     const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
+    const uint32_t lane_mask = (lo < M) ? 0xFFFFFFFFu : 0u;
     const int red_block = (p.waves_k - 1) * M * NB;
 
     // acc[t][v] holds C[m = 4*hi + v][row = row block base + rlw + 16*t + lo]
@@ -608,22 +628,36 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             if (t0 + i < T) {
-                // transpose this step's B (16 rows x 16 chunks per tile) through LDS
+                // transpose this step's B (and A) through the wave's LDS tiles
 #pragma unroll
                 for (int t = 0; t < G; ++t)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) tile[t * 256 + tile_slot(4 * q + hi, lo)] = buf[i][t][q];
+                if constexpr (AG) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                        if (q < aq) {
+                            v = abuf[i][q];
+                            v.x &= amask[q];
+                            v.y &= amask[q];
+                            v.z &= amask[q];
+                            v.w &= amask[q];
+                        }
+                        tile[G * 256 + tile_slot(4 * q + hi, lo)] = v;
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     uint4 a;
                     if constexpr (AG) {
-                        a = abuf[i][s];
-                        a.x &= amask;
-                        a.y &= amask;
-                        a.z &= amask;
-                        a.w &= amask;
+                        a = tile[G * 256 + tile_slot(lo, 4 * s + hi)];
                     } else {
                         a = lds16(ap + (cst * 4 + s) * (64 * kChunk));
+                        a.x &= lane_mask;
+                        a.y &= lane_mask;
+                        a.z &= lane_mask;
+                        a.w &= lane_mask;
                     }
                     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll

@@ -60,7 +60,7 @@ def _configs():
                 MK(inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF),
                 MK(inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=3, depth=PF, rb_per_wg=2),
                 MK(inner=GA, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
-                MK(inner=GA, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF, rb_per_wg=3),
+                MK(inner=GA, split_k=1, row_tiles=G, waves_n=2, waves_k=2, depth=PF, rb_per_wg=3),
                 MK(inner=GA, split_k=3, row_tiles=G, waves_n=1, waves_k=2, depth=PF)]
     return out
 
