@@ -65,9 +65,11 @@ typedef enum { SKG_OUT_F32 = 0, SKG_OUT_BF16 = 1 } skg_out_dtype;
 
 typedef enum {
     SKG_BACKEND_DOT = 0,   /* each workgroup covers all of K for its blocks of rows of B */
-    SKG_BACKEND_SPLITK = 1 /* split_k workgroups per row block, each one slice of K;
-                              fp32 partials are summed in a fixed order by the
-                              last workgroup to finish (no spin-wait) */
+    SKG_BACKEND_SPLITK = 1, /* split_k workgroups per row block, each one slice of K;
+                               fp32 partials are summed in a fixed order by the
+                               last workgroup to finish (no spin-wait) */
+    SKG_BACKEND_SPLITK_2PASS = 2 /* as SPLITK, but a second kernel on the same
+                                    stream sums the partials in split order */
 } skg_backend;
 
 typedef enum {
@@ -86,7 +88,7 @@ typedef enum {
  * skinny_gemm_bf16_with_config accepts.  Plain data; compare field by field. */
 typedef struct skg_config {
     int32_t backend;   /* skg_backend; SKG_BACKEND_DOT requires split_k == 1,
-                          SKG_BACKEND_SPLITK requires split_k >= 2 */
+                          the split-K backends require split_k >= 2 */
     int32_t inner;     /* skg_inner */
     int32_t split_k;   /* workgroups along K per row block */
     int32_t row_tiles; /* rows per wave: VALU 4*row_tiles (1, 2, 4);
@@ -142,8 +144,8 @@ int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
 /* Whether cfg can run (M, K, N): SKG_OK or SKG_ERR_INVALID_ARG.  Pure host. */
 int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg);
 
-/* Bytes of split-K workspace (partials + tickets) cfg needs for (M, K, N);
- * 0 for SKG_BACKEND_DOT.  Pure host. */
+/* Bytes of split-K workspace (partials, plus tickets for SKG_BACKEND_SPLITK)
+ * cfg needs for (M, K, N); 0 for SKG_BACKEND_DOT.  Pure host. */
 int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg,
                                 size_t *bytes);
 

@@ -181,6 +181,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.nck = g.nck;
     p.nfull = g.nfull;
     p.split_k = cfg.split_k;
+    p.two_pass = (cfg.backend == SKG_BACKEND_SPLITK_2PASS);
     p.wg_chunks = g.wg_chunks;
     p.wave_chunks = g.wave_chunks;
     p.waves_n = cfg.waves_n;
@@ -207,7 +208,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (M < 1 || M > SKG_MAX_M || K < 0 || N < 1) return false;
     if (cfg.backend == SKG_BACKEND_DOT) {
         if (cfg.split_k != 1) return false;
-    } else if (cfg.backend == SKG_BACKEND_SPLITK) {
+    } else if (cfg.backend == SKG_BACKEND_SPLITK || cfg.backend == SKG_BACKEND_SPLITK_2PASS) {
         if (cfg.split_k < 2 || cfg.split_k > 4096) return false;
     } else {
         return false;
@@ -252,7 +253,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
     r.threads = 64 * cfg.waves_n * cfg.waves_k;
     r.ws_floats = (S > 1) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
-    r.n_tickets = (S > 1) ? (size_t)r.num_rb : 0;
+    r.n_tickets = (S > 1 && cfg.backend == SKG_BACKEND_SPLITK) ? (size_t)r.num_rb : 0;
     if ((int64_t)r.grid_rb * S > 0x7FFFFFFF) return false;
     *g = r;
     return true;

@@ -399,6 +399,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
                     if (row0 + 4 * r < p.N) store_c(p, m_out, row0 + 4 * r, res[r]);
+        } else if (p.two_pass) {
+            if (wk == 0 && writer) {
+                float *dst = p.ws + ((size_t)(rb * p.split_k + w.s) * M + m_out) * NB;
+#pragma unroll
+                for (int r = 0; r < R; ++r) dst[rl0 + 4 * r] = res[r];
+            }
         } else {
             if (wk == 0) {
                 if (writer) {
@@ -607,6 +613,17 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                         if (m < M && row < p.N) store_c(p, m, row, acc[t][v]);
                     }
                 }
+        } else if (p.two_pass) {
+            if (wk == 0) {
+                float *dst = p.ws + (size_t)(rb * p.split_k + w.s) * M * NB;
+#pragma unroll
+                for (int t = 0; t < G; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = 4 * hi + v;
+                        if (m < M) dst[m * NB + rlw + 16 * t + lo] = acc[t][v];
+                    }
+            }
         } else {
             if (wk == 0) {
                 float *dst = p.ws + (size_t)(rb * p.split_k + w.s) * M * NB;

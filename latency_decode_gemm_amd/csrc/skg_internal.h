@@ -32,6 +32,7 @@ struct KParams {
     int nck;          // ceil(K / 8)
     int nfull;        // K / 8 (chunks with all 8 elements inside K)
     int split_k;      // workgroups along K per row block
+    int two_pass;     // split-K partials are summed by a second kernel
     int wg_chunks;    // chunks per split (multiple of wave_chunks)
     int wave_chunks;  // chunks per K-wave (multiple of the K-step)
     int waves_n, waves_k;

@@ -23,6 +23,29 @@ __global__ void skg_zero_fill_kernel(void *C, int M, int N, int64_t ldc, int out
     }
 }
 
+// Second pass of SKG_BACKEND_SPLITK_2PASS: C[m][row] = sum over s (in split
+// order) of ws[((rb*S + s)*M + m)*NB + rl]; consecutive threads take
+// consecutive rows, so partial reads and C writes are coalesced.
+__global__ void skg_splitk_reduce_kernel(KParams p) {
+    const int NB = p.rows_per_wg;
+    const int per_rb = p.M * NB;
+    const int64_t total = (int64_t)p.num_rb * per_rb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int rb = (int)(i / per_rb);
+        const int rem = (int)(i - (int64_t)rb * per_rb);
+        const int m = rem / NB;
+        const int rl = rem - m * NB;
+        const int row = rb * NB + rl;
+        if (row < p.N) {
+            const float *src = p.ws + (size_t)rb * p.split_k * per_rb + rem;
+            float v = 0.0f;
+            for (int s = 0; s < p.split_k; ++s) v += src[(size_t)s * per_rb];
+            store_c(p, m, row, v);
+        }
+    }
+}
+
 struct MfmaVariant {
     int G, PF;
     KernelPtr lds_a;     // activations staged in LDS
@@ -74,13 +97,24 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
         }
     }
     const unsigned grid = (unsigned)g.grid_rb * (unsigned)cfg.split_k;
+    const bool second = p.two_pass != 0;
+    const int64_t red_total = (int64_t)p.num_rb * p.M * p.rows_per_wg;
+    const unsigned red_grid = (unsigned)std::min<int64_t>((red_total + 255) / 256, 2048);
     if (start || stop) {
+        // the dispatches record the kernels' own start (first kernel) and end
+        // (last kernel)
         KParams arg = p;
         void *args[] = {&arg};
-        return hipExtLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(g.threads),
-                                  args, g.lds_bytes, stream, start, stop, 0);
+        hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid),
+                                          dim3(g.threads), args, g.lds_bytes, stream, start,
+                                          second ? nullptr : stop, 0);
+        if (e != hipSuccess || !second) return e;
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(skg_splitk_reduce_kernel),
+                                  dim3(red_grid), dim3(256), args, 0, stream, nullptr, stop, 0);
     }
     hipLaunchKernelGGL(fn, dim3(grid), dim3(g.threads), g.lds_bytes, stream, p);
+    if (second)
+        hipLaunchKernelGGL(skg_splitk_reduce_kernel, dim3(red_grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

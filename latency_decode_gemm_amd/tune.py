@@ -51,14 +51,15 @@ def structures(skg, M, K, N, inner_set):
                         rpw = max(1, round(num_rb * S / tgt))
                         grids.add(rpw)
                     for rpw in sorted(grids):
-                        cfg = skg.SkgConfig.make(inner=inner, split_k=S, row_tiles=rt, waves_n=wn,
-                                                 waves_k=wk, depth=d, rb_per_wg=rpw)
-                        if not skg.skinny_gemm_check_config(M, K, N, cfg):
-                            continue
                         grid = math.ceil(num_rb / rpw) * S
                         if grid < 32 or grid > 16384:
                             continue
-                        out.append(cfg)
+                        for be in ((0,) if S == 1 else (1, 2)):
+                            cfg = skg.SkgConfig.make(backend=be, inner=inner, split_k=S,
+                                                     row_tiles=rt, waves_n=wn, waves_k=wk,
+                                                     depth=d, rb_per_wg=rpw)
+                            if skg.skinny_gemm_check_config(M, K, N, cfg):
+                                out.append(cfg)
     return out
 
 
@@ -70,8 +71,9 @@ def variants_of(skg, M, K, N, cfg):
         for f in (0.5, 0.75, 1.0, 1.5, 2.0):
             rpw = max(1, int(round(cfg.rb_per_wg * f * rows_per_wave(cfg.inner, cfg.row_tiles)
                                    / rows_per_wave(cfg.inner, rt))))
-            c = skg.SkgConfig.make(inner=cfg.inner, split_k=cfg.split_k, row_tiles=rt,
-                                   waves_n=cfg.waves_n, waves_k=cfg.waves_k, depth=d, rb_per_wg=rpw)
+            c = skg.SkgConfig.make(backend=cfg.backend, inner=cfg.inner, split_k=cfg.split_k,
+                                   row_tiles=rt, waves_n=cfg.waves_n, waves_k=cfg.waves_k,
+                                   depth=d, rb_per_wg=rpw)
             if skg.skinny_gemm_check_config(M, K, N, c):
                 out.append(c)
     return out

@@ -115,6 +115,11 @@ def test_workspace_bytes():
     rows = 4
     nrb = 256 // rows
     assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, sk) == nrb * 4 * 4 * rows * 4 + nrb * 4
+    p2 = skg.SkgConfig.make(backend=skg.SKG_BACKEND_SPLITK_2PASS, split_k=4, row_tiles=1,
+                            waves_k=4)
+    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, p2) == nrb * 4 * 4 * rows * 4
+    bad = skg.SkgConfig.make(backend=skg.SKG_BACKEND_SPLITK_2PASS, split_k=1, row_tiles=1)
+    assert not skg.skinny_gemm_check_config(4, 7168, 256, bad)
 
 
 def test_warmup_keys_first_seen_order():

@@ -46,6 +46,8 @@ def test_split_k_forced_is_reproducible():
     torch = gu.torch_cuda()
     A, B = _problem(16, 7168, 256)
     for cfg in (MK(inner=skg.SKG_INNER_MFMA, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=2),
+                MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=skg.SKG_INNER_MFMA_GA, split_k=4,
+                   row_tiles=1, waves_n=1, waves_k=2, depth=2),
                 MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2, depth=4)):
         ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))
         for _ in range(100):

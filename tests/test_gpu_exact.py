@@ -27,13 +27,17 @@ FAMILIES = [
     MK(inner=F, split_k=4, row_tiles=4, waves_n=1, waves_k=2, depth=1),
     MK(inner=GA, split_k=1, row_tiles=1, waves_n=1, waves_k=4, depth=3, rb_per_wg=2),
     MK(inner=GA, split_k=2, row_tiles=2, waves_n=2, waves_k=1, depth=1),
+    MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=GA, split_k=3, row_tiles=1, waves_n=1,
+       waves_k=2, depth=2),
+    MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=V, split_k=2, row_tiles=2, waves_n=1,
+       waves_k=2, depth=4),
 ]
 
 
 def _fid(c):
     if c is None:
         return "dispatch"
-    return {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
+    return ("p2_" if c.backend == 2 else "") + {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
 
 
