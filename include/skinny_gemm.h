@@ -97,9 +97,10 @@ typedef struct skg_config {
     int32_t waves_k;   /* waves per workgroup on different K slices of the same
                           rows (combined through LDS); waves_n*waves_k <= 8 */
     int32_t depth;     /* 128-wide K steps of loads kept in flight per wave.
-                          Compiled (row_tiles, depth) pairs: VALU (1,4) (1,8) (2,2)
-                          (2,4) (4,2) (4,4); MFMA and MFMA_GA (1,2) (1,3) (1,4)
-                          (2,1) (2,2) (4,1) */
+                          Compiled (row_tiles, depth) pairs: VALU (1,4) (1,8)
+                          (1,12) (2,2) (2,4) (2,8) (4,2) (4,4); MFMA and MFMA_GA
+                          (1,2) (1,3) (1,4) (1,6) (2,1) (2,2) (2,3) (2,4) (4,1)
+                          (4,2) */
     int32_t rb_per_wg; /* row blocks (of rows_per_wave*waves_n rows) each workgroup
                           streams one after another, >= 1; sets the grid size */
 } skg_config;

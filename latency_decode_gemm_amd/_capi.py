@@ -32,8 +32,9 @@ SKG_INNER_MFMA_GA = 2
 SKG_MAX_M = 16
 
 # Compiled (row_tiles, depth) pairs per inner product (the library's tables).
-VALU_VARIANTS = ((1, 4), (1, 8), (2, 2), (2, 4), (4, 2), (4, 4))
-MFMA_VARIANTS = ((1, 2), (1, 3), (1, 4), (2, 1), (2, 2), (4, 1))
+VALU_VARIANTS = ((1, 4), (1, 8), (1, 12), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4))
+MFMA_VARIANTS = ((1, 2), (1, 3), (1, 4), (1, 6), (2, 1), (2, 2), (2, 3), (2, 4), (4, 1),
+                 (4, 2))
 
 # Every function the header declares, with (restype, argtypes).
 _i = ctypes.c_int

@@ -79,6 +79,8 @@ skg_config default_config(int M, int K, int N) {
         c.backend = (c.split_k > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
     }
     while (!make_geometry(M, K, N, c, &g) && c.waves_k > 1) c.waves_k /= 2;
+    // the stash holds rb_per_wg row blocks: more workgroups if it does not fit
+    while (!make_geometry(M, K, N, c, &g) && c.rb_per_wg > 1) c.rb_per_wg /= 2;
     return c;
 }
 
@@ -164,8 +166,6 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
                    ? SKG_OK
                    : SKG_ERR_HIP;
     }
-    Geometry g;
-    if (!make_geometry(M, K, N, cfg, &g)) return SKG_ERR_INVALID_ARG;
     KParams p;
     std::memset(&p, 0, sizeof p);
     p.A = reinterpret_cast<const uint16_t *>(A);
@@ -178,6 +178,10 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.N = N;
     p.K = K;
     p.out_bf16 = (out_dtype == SKG_OUT_BF16);
+    if (K < kChunk)  // rows shorter than one 16-byte window
+        return launch_small_k(p, stream, start, stop) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
+    Geometry g;
+    if (!make_geometry(M, K, N, cfg, &g)) return SKG_ERR_INVALID_ARG;
     p.nck = g.nck;
     p.nfull = g.nfull;
     p.split_k = cfg.split_k;
@@ -189,7 +193,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.rows_per_wg = g.rows_per_wg;
     p.num_rb = g.num_rb;
     p.lds_stride = g.lds_stride;
-    p.red_offset = g.red_offset;
+    p.stash_offset = g.stash_offset;
     p.flag_offset = g.flag_offset;
     p.tr_offset = g.tr_offset;
     if (cfg.split_k > 1) {
@@ -246,9 +250,15 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
                       : (cfg.inner == SKG_INNER_MFMA) ? cfg.row_tiles
                                                       : cfg.row_tiles + 1;
     const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
-    r.red_offset = (int)(r.tr_offset + tr_bytes);
-    const size_t red_bytes = 2 * (size_t)(cfg.waves_k - 1) * M * r.rows_per_wg * sizeof(float);
-    r.flag_offset = (int)(r.red_offset + red_bytes);
+    r.stash_offset = (int)(r.tr_offset + tr_bytes);
+    // stash: every wave's partial sums of each of the workgroup's row blocks
+    // (VALU: M x its rows; MFMA: one 16 x 16 fp32 tile per 16 rows)
+    const size_t per_block = (cfg.inner == SKG_INNER_VALU) ? (size_t)M * r.rows_per_wg
+                                                           : (size_t)16 * r.rows_per_wg;
+    const size_t blocks_per_wg = (size_t)ceil_div(r.num_rb, r.grid_rb);
+    const size_t stash_bytes = blocks_per_wg * cfg.waves_k * per_block * sizeof(float);
+    if (r.stash_offset + stash_bytes > (size_t)kMaxLdsBytes) return false;
+    r.flag_offset = (int)(r.stash_offset + stash_bytes);
     r.lds_bytes = r.flag_offset + 16;
     if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
     r.threads = 64 * cfg.waves_n * cfg.waves_k;

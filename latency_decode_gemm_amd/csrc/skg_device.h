@@ -117,34 +117,40 @@ __device__ __forceinline__ void store_c(const KParams &p, int m, int n, float v)
         reinterpret_cast<float *>(p.C)[off] = v;
 }
 
-// One 8-element chunk (k = 8c .. 8c+7) of the row starting at rowp, with
-// every element at k >= K read as zero (no access beyond K).
-template <bool STREAM = false>
-__device__ __forceinline__ uint4 load_chunk_masked(const uint16_t *rowp, int c, const KParams &p) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (c < p.nfull) {
-        v = STREAM ? ldg16_stream(rowp + (int64_t)c * kChunk) : ldg16(rowp + (int64_t)c * kChunk);
-    } else if (c < p.nck) {
-        // the one chunk that straddles K (K % 8 != 0)
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        const int k0 = c * kChunk;
+// ---- K tail ------------------------------------------------------------------
+// Every load is one 16-byte window.  Chunk c < nfull is read in place.  The
+// chunk that straddles K (K % 8 != 0) is read as the window ending exactly at
+// K, and chunks beyond K re-read that same window, so no load ever leaves
+// [0, K) of its row (K >= 8; smaller K has a kernel of its own).  The mask
+// below then keeps only what belongs to chunk c: all of it for c < nfull,
+// the last K % 8 elements for the straddling chunk, nothing beyond K.  Both
+// operands are masked, so padding (even NaN) never meets a product.
+__device__ __forceinline__ int64_t window_off(int c, const KParams &p) {
+    return (int64_t)min(c * kChunk, p.K - kChunk);
+}
+
+__device__ __forceinline__ uint4 tail_mask(int c, const KParams &p) {
+    const int j0 = (c < p.nfull) ? 0 : (c < p.nck ? kChunk - (p.K - p.nfull * kChunk) : kChunk);
+    uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-            if (k0 + e < p.K) {
-                const uint32_t h = rowp[k0 + e];
-                w[e >> 1] |= h << (16 * (e & 1));
-            }
-        }
-        v = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    return v;
+    for (int d = 0; d < 4; ++d)
+        w[d] = ((2 * d >= j0) ? 0x0000FFFFu : 0u) | ((2 * d + 1 >= j0) ? 0xFFFF0000u : 0u);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 and4(uint4 v, uint4 m) {
+    return make_uint4(v.x & m.x, v.y & m.y, v.z & m.z, v.w & m.w);
+}
+
+// Chunk c of the row at rowp as the kernels see it (window + mask).
+__device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *rowp, int c, const KParams &p) {
+    return and4(ldg16(rowp + window_off(c, p)), tail_mask(c, p));
 }
 
 // Stage A[m, 8*wg_c0 : 8*(wg_c0 + wg_chunks)) for m < M into LDS rows of
-// p.lds_stride elements; zeros beyond K.  Each wave moves blocks of 64 chunks
-// (1 KB, one row) straight into LDS; the chunk straddling K and the chunks
-// beyond it are written as (partial) zeros by ordinary LDS stores.  The
-// caller's barrier waits for all of it.
+// p.lds_stride elements.  Each wave moves blocks of 64 chunks (1 KB, one row)
+// straight into LDS; chunks from nfull on are written by ordinary LDS stores
+// in the tail form above.  The caller's barrier waits for all of it.
 __device__ __forceinline__ void stage_a(const KParams &p, uint16_t *As, int wg_c0) {
     const int lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -161,7 +167,7 @@ __device__ __forceinline__ void stage_a(const KParams &p, uint16_t *As, int wg_c
             if (c < p.nfull)
                 lds_dma16(rowp + (int64_t)c * kChunk, dst);
             else
-                sts16(dst + lane * kChunk, load_chunk_masked(rowp, c, p));
+                sts16(dst + lane * kChunk, load_chunk_tail(rowp, c, p));
         }
     }
 }
@@ -299,6 +305,43 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
     return w;
 }
 
+// ---- epilogue ------------------------------------------------------------------
+// After its stream, a workgroup holds in LDS (the stash) each wave's partial
+// sums of each of its row blocks.  Its threads then take the outputs of a row
+// block in (m, row) order, add the waves_k partials in wave order, and write
+// C (split_k == 1) or the split's partial (split_k > 1; the single-pass
+// backend then settles the row block with splitk_complete).  IDX maps (row
+// block b, K-wave q, token m, local row rl) to the stash index.
+template <class IDX>
+__device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, const float *stash,
+                                             unsigned *flag, IDX idx) {
+    __syncthreads();
+    const int NB = p.rows_per_wg;
+    const int total = p.M * NB;
+    for (int b = 0; b < w.nblk; ++b) {
+        const int rb = w.rb0 + b * w.rbs;
+        float *part = (p.split_k > 1) ? p.ws + (size_t)(rb * p.split_k + w.s) * total : nullptr;
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            const int m = i / NB;
+            const int rl = i - m * NB;
+            float v = stash[idx(b, 0, m, rl)];
+            for (int q = 1; q < p.waves_k; ++q) v += stash[idx(b, q, m, rl)];
+            if (p.split_k == 1) {
+                const int row = rb * NB + rl;
+                if (row < p.N) store_c(p, m, row, v);
+            } else if (p.two_pass) {
+                part[i] = v;
+            } else {
+                ws_store(part + i, v);
+            }
+        }
+        if (p.split_k > 1 && !p.two_pass) {
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores complete
+            splitk_complete(p, rb, flag);
+        }
+    }
+}
+
 // ---- VALU kernel --------------------------------------------------------------
 // M: tokens (compile time); R: row slots per wave (4 rows each);
 // PF: K-steps of B loads in flight (register ring depth).
@@ -306,11 +349,11 @@ template <int M, int R, int PF>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
-    float *red = reinterpret_cast<float *>(smem + p.red_offset);
+    float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
     unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int l16 = lane & 15;
     const int slot = lane >> 4;
     const int wk = wave / p.waves_n;
@@ -320,38 +363,34 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     const int SPB = p.wave_chunks / kValuStep;  // K steps per row block
     const int T = w.nblk * SPB;
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
+    // first step of the slice that reaches past the last full chunk
+    const int tail_st = max(0, (p.nfull - wv_c0) / kValuStep);
     const int rl0 = wn * (4 * R) + slot;  // local row of slot r = 0
 
-    // load cursor: row block lb, step lst
+    // load cursor: row block lb, step lst; once past the last row block the
+    // loads read row 0 of A instead (in bounds, cache-resident, never used)
     int lb = 0, lst = 0;
     const uint16_t *rowp[R];
     auto set_rows = [&](int b) {
         const int rbase = (w.rb0 + b * w.rbs) * NB + rl0;
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            rowp[r] = p.B + (int64_t)min(rbase + 4 * r, p.N - 1) * p.ldb;
+            rowp[r] = (b < w.nblk) ? p.B + (int64_t)min(rbase + 4 * r, p.N - 1) * p.ldb : p.A;
     };
     auto issue = [&](uint4(&dst)[R]) {
-        const int cb = wv_c0 + lst * kValuStep;
-        const int c = cb + l16;
-        if (cb + kValuStep <= p.nfull) {
+        const int64_t off = window_off(wv_c0 + lst * kValuStep + l16, p);
 #pragma unroll
-            for (int r = 0; r < R; ++r) dst[r] = ldg16_stream(rowp[r] + (int64_t)c * kChunk);
-        } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r) dst[r] = load_chunk_masked<true>(rowp[r], c, p);
-        }
+        for (int r = 0; r < R; ++r) dst[r] = ldg16_stream(rowp[r] + off);
         if (++lst == SPB) {
             lst = 0;
-            if (++lb < w.nblk) set_rows(lb);
+            set_rows(++lb);
         }
     };
 
     uint4 buf[PF][R];
-    if (w.nblk > 0) set_rows(0);
+    set_rows(0);
 #pragma unroll
-    for (int i = 0; i < PF; ++i)
-        if (i < T) issue(buf[i]);
+    for (int i = 0; i < PF; ++i) issue(buf[i]);
 
     stage_a(p, As, w.wg_c0);
     __syncthreads();
@@ -364,86 +403,58 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 
     constexpr int VP = Pow2Ceil<M>::v;
     const bool writer = l16 < M;
-    const int m_out = l16;
     const uint16_t *ap = As + (wk * p.wave_chunks + l16) * kChunk;
-    const int red_block = (p.waves_k - 1) * M * NB;  // floats per red buffer
+    // stash: [row block][K-wave][m][local row]
+    const int per_block = p.waves_k * M * NB;
 
-    // epilogue of compute row block b: reduce, combine waves, write
-    auto finish_block = [&](int b) {
-        float res[R];
+    int cb = 0, cst = 0;  // compute cursor
+    auto step = [&](uint4(&bv)[R]) {
+        if (cst >= tail_st) {
+            const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + l16, p);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float v[VP];
-#pragma unroll
-            for (int j = 0; j < VP; ++j) v[j] = (j < M) ? acc[r][j] : 0.0f;
-            reduce16<VP>(v, lane);
-            res[r] = v[0];
+            for (int r = 0; r < R; ++r) bv[r] = and4(bv[r], mk);
         }
-        const int rb = w.rb0 + b * w.rbs;
-        if (p.waves_k > 1) {
-            float *rbuf = red + (b & 1) * red_block;
-            if (wk > 0 && writer)
+        const uint16_t *a_st = ap + cst * (kValuStep * kChunk);
+        uint4 a[M];
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                    rbuf[((wk - 1) * M + m_out) * NB + rl0 + 4 * r] = res[r];
-            lds_barrier();
-            if (wk == 0 && writer)
-                for (int q = 1; q < p.waves_k; ++q)
+        for (int m = 0; m < M; ++m) a[m] = lds16(a_st + m * p.lds_stride);
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        res[r] += rbuf[((q - 1) * M + m_out) * NB + rl0 + 4 * r];
-        }
-        const int row0 = rb * NB + rl0;
-        if (p.split_k == 1) {
-            if (wk == 0 && writer)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (row0 + 4 * r < p.N) store_c(p, m_out, row0 + 4 * r, res[r]);
-        } else if (p.two_pass) {
-            if (wk == 0 && writer) {
-                float *dst = p.ws + ((size_t)(rb * p.split_k + w.s) * M + m_out) * NB;
+            for (int m = 0; m < M; ++m) acc[r][m] = dot8(a[m], bv[r], acc[r][m]);
+        if (++cst == SPB) {
+            // row block done: lane m of each row group now takes token m
+            float *dst = stash + cb * per_block + (wk * M + l16) * NB + rl0;
 #pragma unroll
-                for (int r = 0; r < R; ++r) dst[rl0 + 4 * r] = res[r];
+            for (int r = 0; r < R; ++r) {
+                float v[VP];
+#pragma unroll
+                for (int j = 0; j < VP; ++j) v[j] = (j < M) ? acc[r][j] : 0.0f;
+                reduce16<VP>(v, lane);
+                if (writer) dst[4 * r] = v[0];
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
             }
-        } else {
-            if (wk == 0) {
-                if (writer) {
-                    float *dst = p.ws + ((size_t)(rb * p.split_k + w.s) * M + m_out) * NB;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) ws_store(dst + rl0 + 4 * r, res[r]);
-                }
-                __builtin_amdgcn_s_waitcnt(0);  // partial stores complete
-            }
-            splitk_complete(p, rb, flag);
+            cst = 0;
+            ++cb;
         }
     };
 
-    int cb = 0, cst = 0;  // compute cursor
-    for (int t0 = 0; t0 < T; t0 += PF) {
+    // Whole rounds of the ring: every slot is refilled unconditionally right
+    // after it is consumed, so the compiler keeps each slot in the same
+    // registers and waits for exactly that slot's loads.  Steps past T only
+    // refill (from A, see set_rows).
+    const int TT = (T + PF - 1) / PF * PF;
+    for (int t0 = 0; t0 < TT; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (t0 + i < T) {
-                const uint16_t *a_st = ap + cst * (kValuStep * kChunk);
-                uint4 a[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) a[m] = lds16(a_st + m * p.lds_stride);
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int m = 0; m < M; ++m) acc[r][m] = dot8(a[m], buf[i][r], acc[r][m]);
-                if (t0 + i + PF < T) issue(buf[i]);
-                if (++cst == SPB) {
-                    finish_block(cb);
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-#pragma unroll
-                        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-                    cst = 0;
-                    ++cb;
-                }
-            }
+            if (t0 + i < T) step(buf[i]);
+            issue(buf[i]);
         }
     }
+    write_blocks(p, w, stash, flag, [&](int b, int q, int m, int rl) {
+        return (b * p.waves_k + q) * M * NB + m * NB + rl;
+    });
 }
 
 // ---- MFMA kernel ------------------------------------------------------------
@@ -465,7 +476,7 @@ __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int
         if (c < p.nfull)
             lds_dma16(rowp + (int64_t)c * kChunk, dst);
         else
-            sts16(dst + lane * kChunk, load_chunk_masked(rowp, c, p));
+            sts16(dst + lane * kChunk, load_chunk_tail(rowp, c, p));
     }
 }
 
@@ -479,20 +490,24 @@ __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int
 // reads (16 rows, one chunk each per quarter-wave) both hit 16 distinct slots.
 __device__ __forceinline__ int tile_slot(int r, int c) { return r * 16 + (c ^ r); }
 
-// G: 16-row tiles per wave; PF: 128-wide K steps of loads in flight; AG: the
-// activations of each step are loaded from global memory (L2-resident, in the
-// same register ring as B, with the same row-segment layout) and transposed
-// through their own wave-private tile, instead of being staged in LDS.
-// M <= 16 at run time (activation rows m >= M are fed as zeros).
-template <int G, int PF, bool AG>
+// G: 16-row tiles per wave; PF: 128-wide K steps of loads in flight; AQ: 0
+// when the activations are staged in LDS, else the number of activation loads
+// per step (rows 4q + (lane >> 4), q < AQ: AQ = 4 covers M <= 16, AQ = 2
+// covers M <= 8): the activations are then loaded from global memory
+// (L2-resident), in the same ring and row-segment layout as B, and transposed
+// through their own wave-private tile.  M <= 16 at run time (activation rows
+// m >= M are fed as zeros).
+template <int G, int PF, int AQ>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
+    constexpr bool AG = AQ > 0;
+    constexpr int NA = AG ? AQ : 1;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
-    float *red = reinterpret_cast<float *>(smem + p.red_offset);
+    float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
     unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lo = lane & 15;  // load: chunk within the step; operand: row / token
     const int hi = lane >> 4;  // load: row within a group of 4; operand: chunk of 4
     const int wk = wave / p.waves_n;
@@ -503,68 +518,61 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     const int SPB = p.wave_chunks / kValuStep;
     const int T = w.nblk * SPB;
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
-    const int rlw = wn * (16 * G);  // first local row of this wave
+    const int tail_st = max(0, (p.nfull - wv_c0) / kValuStep);
     constexpr int NT = G + (AG ? 1 : 0);  // transpose tiles per wave (B tiles, then A)
     uint4 *tile = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (NT * 256);
     // AG: activation rows 4q + hi of this lane (rows >= M read row M-1, masked)
-    const int aq = (M + 3) >> 2;  // activation loads per step
-    const uint16_t *arow[4];
-    uint32_t amask[4];
+    const uint16_t *arow[NA];
+    uint4 amask[NA];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NA; ++q) {
         arow[q] = p.A + (int64_t)min(4 * q + hi, M - 1) * p.lda;
-        amask[q] = (4 * q + hi < M) ? 0xFFFFFFFFu : 0u;
+        const uint32_t mq = (4 * q + hi < M) ? 0xFFFFFFFFu : 0u;
+        amask[q] = make_uint4(mq, mq, mq, mq);
     }
 
+    // load cursor; past the last row block the B loads read row 0 of A
     int lb = 0, lst = 0;
     const uint16_t *rowp[G][4];
     auto set_rows = [&](int b) {
-        const int rbase = (w.rb0 + b * w.rbs) * NB + rlw + hi;
+        const int rbase = (w.rb0 + b * w.rbs) * NB + wn * (16 * G) + hi;
 #pragma unroll
         for (int t = 0; t < G; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                rowp[t][q] = p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb;
+                rowp[t][q] = (b < w.nblk)
+                                 ? p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb
+                                 : p.A;
     };
-    auto issue = [&](uint4(&dst)[G][4], uint4(&adst)[4]) {
-        const int cb = wv_c0 + lst * kValuStep;
-        const int c = cb + lo;
-        if (cb + kValuStep <= p.nfull) {
+    auto issue = [&](uint4(&dst)[G][4], uint4(&adst)[NA]) {
+        const int64_t off = window_off(wv_c0 + lst * kValuStep + lo, p);
 #pragma unroll
-            for (int t = 0; t < G; ++t)
+        for (int t = 0; t < G; ++t)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    dst[t][q] = ldg16_stream(rowp[t][q] + (int64_t)c * kChunk);
-            if constexpr (AG)
+            for (int q = 0; q < 4; ++q) dst[t][q] = ldg16_stream(rowp[t][q] + off);
+        if constexpr (AG)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (q < aq) adst[q] = ldg16(arow[q] + (int64_t)c * kChunk);
-        } else {
-#pragma unroll
-            for (int t = 0; t < G; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) dst[t][q] = load_chunk_masked<true>(rowp[t][q], c, p);
-            if constexpr (AG)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (q < aq) adst[q] = load_chunk_masked(arow[q], c, p);
-        }
+            for (int q = 0; q < AQ; ++q) adst[q] = ldg16(arow[q] + off);
         if (++lst == SPB) {
             lst = 0;
-            if (++lb < w.nblk) set_rows(lb);
+            set_rows(++lb);
         }
     };
 
     uint4 buf[PF][G][4];
-    uint4 abuf[PF][4];
-    if (w.nblk > 0) set_rows(0);
+    uint4 abuf[PF][NA];
+    set_rows(0);
 #pragma unroll
-    for (int i = 0; i < PF; ++i)
-        if (i < T) issue(buf[i], abuf[i]);
+    for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
 
     if constexpr (!AG) {
         stage_a_frag(p, As, w.wg_c0);
         __syncthreads();
+    } else {
+        // activation rows 4 * AQ .. 15 of the A tile stay zero
+#pragma unroll
+        for (int q = AQ; q < 4; ++q)
+            tile[G * 256 + tile_slot(4 * q + hi, lo)] = make_uint4(0u, 0u, 0u, 0u);
     }
 
     f32x4_t acc[G];
@@ -575,132 +583,85 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     // lanes of tokens m >= M zero what they read
     const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
     const uint32_t lane_mask = (lo < M) ? 0xFFFFFFFFu : 0u;
-    const int red_block = (p.waves_k - 1) * M * NB;
+    // stash: [row block][K-wave][N-wave][tile] blocks of 64 lanes x 4 floats;
+    // lane 16*hi + lo, element v holds token 4*hi + v, row 16*tile + lo
+    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * 64 + lane;
+    const int st_block = p.waves_k * p.waves_n * G * 64;  // f32x4 per row block
 
-    // acc[t][v] holds C[m = 4*hi + v][row = row block base + rlw + 16*t + lo]
-    auto finish_block = [&](int b) {
-        const int rb = w.rb0 + b * w.rbs;
-        if (p.waves_k > 1) {
-            float *rbuf = red + (b & 1) * red_block;
-            if (wk > 0)
+    int cb = 0, cst = 0;
+    auto step = [&](uint4(&bv)[G][4], uint4(&av)[NA]) {
+        if (cst >= tail_st) {
+            const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + lo, p);
 #pragma unroll
-                for (int t = 0; t < G; ++t)
+            for (int t = 0; t < G; ++t)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * hi + v;
-                        if (m < M) rbuf[((wk - 1) * M + m) * NB + rlw + 16 * t + lo] = acc[t][v];
-                    }
-            lds_barrier();
-            if (wk == 0)
-                for (int q = 1; q < p.waves_k; ++q)
+                for (int q = 0; q < 4; ++q) bv[t][q] = and4(bv[t][q], mk);
+            if constexpr (AG)
 #pragma unroll
-                    for (int t = 0; t < G; ++t)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int m = 4 * hi + v;
-                            if (m < M) acc[t][v] += rbuf[((q - 1) * M + m) * NB + rlw + 16 * t + lo];
-                        }
+                for (int q = 0; q < AQ; ++q) av[q] = and4(av[q], mk);
         }
-        const int rowb = rb * NB + rlw + lo;
-        if (p.split_k == 1) {
-            if (wk == 0)
+        // transpose this step's B (and A) through the wave's LDS tiles
 #pragma unroll
-                for (int t = 0; t < G; ++t) {
-                    const int row = rowb + 16 * t;
+        for (int t = 0; t < G; ++t)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * hi + v;
-                        if (m < M && row < p.N) store_c(p, m, row, acc[t][v]);
-                    }
-                }
-        } else if (p.two_pass) {
-            if (wk == 0) {
-                float *dst = p.ws + (size_t)(rb * p.split_k + w.s) * M * NB;
+            for (int q = 0; q < 4; ++q) tile[t * 256 + tile_slot(4 * q + hi, lo)] = bv[t][q];
+        if constexpr (AG)
 #pragma unroll
-                for (int t = 0; t < G; ++t)
+            for (int q = 0; q < AQ; ++q)
+                tile[G * 256 + tile_slot(4 * q + hi, lo)] = and4(av[q], amask[q]);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * hi + v;
-                        if (m < M) dst[m * NB + rlw + 16 * t + lo] = acc[t][v];
-                    }
+        for (int s = 0; s < 4; ++s) {
+            uint4 a;
+            if constexpr (AG) {
+                a = tile[G * 256 + tile_slot(lo, 4 * s + hi)];
+            } else {
+                a = lds16(ap + (cst * 4 + s) * (64 * kChunk));
+                a.x &= lane_mask;
+                a.y &= lane_mask;
+                a.z &= lane_mask;
+                a.w &= lane_mask;
             }
-        } else {
-            if (wk == 0) {
-                float *dst = p.ws + (size_t)(rb * p.split_k + w.s) * M * NB;
+            const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-                for (int t = 0; t < G; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * hi + v;
-                        if (m < M) ws_store(dst + m * NB + rlw + 16 * t + lo, acc[t][v]);
-                    }
-                __builtin_amdgcn_s_waitcnt(0);  // partial stores complete
+            for (int t = 0; t < G; ++t) {
+                const uint4 b8 = tile[t * 256 + tile_slot(lo, 4 * s + hi)];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a8, __builtin_bit_cast(bf16x8_t, b8), acc[t], 0, 0, 0);
             }
-            splitk_complete(p, rb, flag);
+        }
+        if (++cst == SPB) {
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+                st[cb * st_block + t * 64] = acc[t];
+                acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            cst = 0;
+            ++cb;
         }
     };
 
-    int cb = 0, cst = 0;
-    for (int t0 = 0; t0 < T; t0 += PF) {
+    // whole rounds of the ring, as in the VALU kernel
+    const int TT = (T + PF - 1) / PF * PF;
+    for (int t0 = 0; t0 < TT; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (t0 + i < T) {
-                // transpose this step's B (and A) through the wave's LDS tiles
-#pragma unroll
-                for (int t = 0; t < G; ++t)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) tile[t * 256 + tile_slot(4 * q + hi, lo)] = buf[i][t][q];
-                if constexpr (AG) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                        if (q < aq) {
-                            v = abuf[i][q];
-                            v.x &= amask[q];
-                            v.y &= amask[q];
-                            v.z &= amask[q];
-                            v.w &= amask[q];
-                        }
-                        tile[G * 256 + tile_slot(4 * q + hi, lo)] = v;
-                    }
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    uint4 a;
-                    if constexpr (AG) {
-                        a = tile[G * 256 + tile_slot(lo, 4 * s + hi)];
-                    } else {
-                        a = lds16(ap + (cst * 4 + s) * (64 * kChunk));
-                        a.x &= lane_mask;
-                        a.y &= lane_mask;
-                        a.z &= lane_mask;
-                        a.w &= lane_mask;
-                    }
-                    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-                    for (int t = 0; t < G; ++t) {
-                        const uint4 bv = tile[t * 256 + tile_slot(lo, 4 * s + hi)];
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            av, __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
-                    }
-                }
-                if (t0 + i + PF < T) issue(buf[i], abuf[i]);
-                if (++cst == SPB) {
-                    finish_block(cb);
-#pragma unroll
-                    for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                    cst = 0;
-                    ++cb;
-                }
-            }
+            if (t0 + i < T) step(buf[i], abuf[i]);
+            issue(buf[i], abuf[i]);
         }
     }
+    write_blocks(p, w, stash, flag, [&](int b, int q, int m, int rl) {
+        const int wq = rl / (16 * G);     // N-wave
+        const int t = (rl >> 4) % G;      // tile
+        const int l = 16 * (m >> 2) + (rl & 15);
+        return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + l * 4 + (m & 3);
+    });
 }
 
 // Instantiation list for one M, in the order of kValuVariants.
-#define SKG_VALU_ROW(M)                                                           \
-    {skg_valu_kernel<M, 1, 4>, skg_valu_kernel<M, 1, 8>, skg_valu_kernel<M, 2, 2>, \
-     skg_valu_kernel<M, 2, 4>, skg_valu_kernel<M, 4, 2>, skg_valu_kernel<M, 4, 4>}
+#define SKG_VALU_ROW(M)                                                             \
+    {skg_valu_kernel<M, 1, 4>, skg_valu_kernel<M, 1, 8>, skg_valu_kernel<M, 1, 12>,  \
+     skg_valu_kernel<M, 2, 2>, skg_valu_kernel<M, 2, 4>, skg_valu_kernel<M, 2, 8>,   \
+     skg_valu_kernel<M, 4, 2>, skg_valu_kernel<M, 4, 4>}
 
 }  // namespace
 }  // namespace skg

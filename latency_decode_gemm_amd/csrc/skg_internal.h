@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI layer (skg_api.cpp) and the gfx950
-// kernels (skg_kernels.hip).  Not installed; not part of the public ABI.
+// kernels (skg_device.h, instantiated in skg_valu_lo.hip, skg_valu_hi.hip and
+// skg_launch.hip).  Not installed; not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,8 +40,8 @@ struct KParams {
     int rows_per_wg;
     int num_rb;
     int lds_stride;   // bf16 elements per staged A row in LDS
-    int red_offset;   // byte offset of the cross-wave reduction area in LDS
-                      // (two buffers of (waves_k-1)*M*rows_per_wg floats)
+    int stash_offset; // byte offset in LDS of the per-row-block partial sums
+                      // that the epilogue combines
     int flag_offset;  // byte offset of the split-K "last arrival" flag in LDS
     int tr_offset;    // byte offset of the MFMA kernel's per-wave transpose tiles
 };
@@ -55,7 +56,7 @@ struct Geometry {
     int threads;
     int lds_stride;    // elements
     size_t lds_bytes;
-    int red_offset, flag_offset, tr_offset;
+    int stash_offset, flag_offset, tr_offset;
     size_t ws_floats;  // split-K partial floats
     size_t n_tickets;
 };
@@ -76,6 +77,11 @@ hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
                             hipStream_t stream, hipEvent_t start = nullptr,
                             hipEvent_t stop = nullptr);
 
+// K in 1..7: one thread per output, plain fp32 sum (p needs A, B, C, lda,
+// ldb, ldc, M, N, K, out_bf16).
+hipError_t launch_small_k(const KParams &p, hipStream_t stream, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
+
 // Loads a kernel's code object (forces lazy loading) for availability checks.
 hipError_t probe_kernels();
 
@@ -86,7 +92,8 @@ constexpr int kTileBytes = 4096;
 // instantiations live in skg_valu_lo.hip (M = 1..8) and skg_valu_hi.hip
 // (M = 9..16), the MFMA ones in skg_launch.hip.
 using KernelPtr = void (*)(KParams);
-constexpr int kValuVariants[][2] = {{1, 4}, {1, 8}, {2, 2}, {2, 4}, {4, 2}, {4, 4}};
+constexpr int kValuVariants[][2] = {{1, 4}, {1, 8}, {1, 12}, {2, 2},
+                                     {2, 4}, {2, 8}, {4, 2}, {4, 4}};
 constexpr int kNumValu = sizeof(kValuVariants) / sizeof(kValuVariants[0]);
 KernelPtr valu_kernel_lo(int M, int variant);
 KernelPtr valu_kernel_hi(int M, int variant);

@@ -23,6 +23,24 @@ __global__ void skg_zero_fill_kernel(void *C, int M, int N, int64_t ldc, int out
     }
 }
 
+// K < 8: every row is shorter than one 16-byte window, so each output is a
+// plain fp32 sum over k of elementwise products (one thread per output).
+__global__ void skg_small_k_kernel(KParams p) {
+    const int64_t total = (int64_t)p.M * p.N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(i / p.N);
+        const int n = (int)(i - (int64_t)m * p.N);
+        const uint16_t *a = p.A + (int64_t)m * p.lda;
+        const uint16_t *b = p.B + (int64_t)n * p.ldb;
+        float v = 0.0f;
+        for (int k = 0; k < p.K; ++k)
+            v = fmaf(__builtin_bit_cast(float, (uint32_t)a[k] << 16),
+                     __builtin_bit_cast(float, (uint32_t)b[k] << 16), v);
+        store_c(p, m, n, v);
+    }
+}
+
 // Second pass of SKG_BACKEND_SPLITK_2PASS: C[m][row] = sum over s (in split
 // order) of ws[((rb*S + s)*M + m)*NB + rl]; consecutive threads take
 // consecutive rows, so partial reads and C writes are coalesced.
@@ -48,12 +66,16 @@ __global__ void skg_splitk_reduce_kernel(KParams p) {
 
 struct MfmaVariant {
     int G, PF;
-    KernelPtr lds_a;     // activations staged in LDS
-    KernelPtr global_a;  // activation fragments loaded from global memory
+    KernelPtr lds_a;  // activations staged in LDS
+    KernelPtr ga2;    // activations loaded from global memory, M <= 8
+    KernelPtr ga4;    // activations loaded from global memory, M <= 16
 };
-#define SKG_MFMA(G, PF) {G, PF, skg_mfma_kernel<G, PF, false>, skg_mfma_kernel<G, PF, true>}
+#define SKG_MFMA(G, PF) \
+    {G, PF, skg_mfma_kernel<G, PF, 0>, skg_mfma_kernel<G, PF, 2>, skg_mfma_kernel<G, PF, 4>}
 const MfmaVariant kMfmaVariants[] = {SKG_MFMA(1, 2), SKG_MFMA(1, 3), SKG_MFMA(1, 4),
-                                     SKG_MFMA(2, 1), SKG_MFMA(2, 2), SKG_MFMA(4, 1)};
+                                     SKG_MFMA(1, 6), SKG_MFMA(2, 1), SKG_MFMA(2, 2),
+                                     SKG_MFMA(2, 3), SKG_MFMA(2, 4), SKG_MFMA(4, 1),
+                                     SKG_MFMA(4, 2)};
 #undef SKG_MFMA
 constexpr int kNumMfma = sizeof(kMfmaVariants) / sizeof(kMfmaVariants[0]);
 
@@ -68,7 +90,8 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
         for (int i = 0; i < kNumMfma; ++i)
             if (kMfmaVariants[i].G == row_tiles && kMfmaVariants[i].PF == depth)
                 return inner == SKG_INNER_MFMA ? kMfmaVariants[i].lds_a
-                                               : kMfmaVariants[i].global_a;
+                       : M <= 8                ? kMfmaVariants[i].ga2
+                                               : kMfmaVariants[i].ga4;
     }
     return nullptr;
 }
@@ -129,6 +152,20 @@ hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
     }
     hipLaunchKernelGGL(skg_zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, C, M, N, ldc,
                        out_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_small_k(const KParams &p, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+    const int64_t total = (int64_t)p.M * p.N;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+    if (start || stop) {
+        KParams arg = p;
+        void *args[] = {&arg};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(skg_small_k_kernel),
+                                  dim3(blocks), dim3(256), args, 0, stream, start, stop, 0);
+    }
+    hipLaunchKernelGGL(skg_small_k_kernel, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

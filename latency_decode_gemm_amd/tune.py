@@ -38,7 +38,7 @@ def rows_per_wave(inner, rt):
 def structures(skg, M, K, N, inner_set):
     """(inner, rt, depth, wn, wk, S, rb_per_wg) tuples for stage 1."""
     out = []
-    mid_depth = {0: {1: 8, 2: 4, 4: 2}, 1: {1: 3, 2: 2, 4: 1}, 2: {1: 3, 2: 2, 4: 1}}
+    mid_depth = {0: {1: 8, 2: 4, 4: 4}, 1: {1: 4, 2: 2, 4: 2}, 2: {1: 4, 2: 2, 4: 2}}
     for inner in inner_set:
         for rt in (1, 2, 4):
             d = mid_depth[inner][rt]

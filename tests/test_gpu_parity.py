@@ -59,7 +59,8 @@ def _configs():
                 MK(backend=P2, inner=V, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF)]
     for (G, PF) in skg._capi.MFMA_VARIANTS:
         out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
-                MK(inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=4, depth=PF),
+                # 8 waves of 4 transpose tiles each would not leave LDS for A
+                MK(inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=4 if G < 4 else 2, depth=PF),
                 MK(inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=3, depth=PF, rb_per_wg=2),
                 MK(inner=GA, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 MK(inner=GA, split_k=1, row_tiles=G, waves_n=2, waves_k=2, depth=PF, rb_per_wg=3),
