@@ -77,9 +77,13 @@ typedef enum {
                               A staged in LDS */
     SKG_INNER_MFMA = 1,    /* 16x16x32 bf16 matrix-core tiles (M padded to 16);
                               A staged in LDS */
-    SKG_INNER_MFMA_GA = 2  /* as SKG_INNER_MFMA, with the activation fragments
+    SKG_INNER_MFMA_GA = 2, /* as SKG_INNER_MFMA, with the activation fragments
                               read from global memory (L2) each K step: no LDS
                               for A, so any K fits in one workgroup */
+    SKG_INNER_VALU_GA = 3  /* as SKG_INNER_VALU, with each K step's activation
+                              chunks read from global memory (L2) into the
+                              load ring: no staging, no LDS for A; M <= 8
+                              and M * depth <= 32 */
 } skg_inner;
 
 #define SKG_MAX_M 16

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskinny_gemm.so")
 
-SOURCES = ["skg_valu_lo.hip", "skg_valu_hi.hip", "skg_launch.hip", "skg_api.cpp"]
+SOURCES = ["skg_valu_lo.hip", "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_launch.hip",
+           "skg_api.cpp"]
 HEADERS = ["skg_device.h", "skg_internal.h", "tuned_table.inc",
            os.path.join("..", "..", "include", "skinny_gemm.h")]
 ARCH = "gfx950"

@@ -218,8 +218,11 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
         return false;
     }
     if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA &&
-        cfg.inner != SKG_INNER_MFMA_GA)
+        cfg.inner != SKG_INNER_MFMA_GA && cfg.inner != SKG_INNER_VALU_GA)
         return false;
+    const bool valu = cfg.inner == SKG_INNER_VALU || cfg.inner == SKG_INNER_VALU_GA;
+    // VALU_GA keeps depth x M activation chunks in registers
+    if (cfg.inner == SKG_INNER_VALU_GA && (M > 8 || M * cfg.depth > 32)) return false;
     if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth)) return false;
     if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
     if (cfg.rb_per_wg < 1) return false;
@@ -227,7 +230,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.step = kValuStep;
     r.nck = ceil_div(K, kChunk);
     r.nfull = K / kChunk;
-    r.rows_per_wave = (cfg.inner == SKG_INNER_VALU) ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
+    r.rows_per_wave = valu ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
     r.rows_per_wg = r.rows_per_wave * cfg.waves_n;
     r.num_rb = ceil_div(N, r.rows_per_wg);
     r.grid_rb = ceil_div(r.num_rb, cfg.rb_per_wg);
@@ -237,7 +240,8 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.wg_chunks = r.wave_chunks * cfg.waves_k;
     if ((int64_t)(S - 1) * r.wg_chunks >= std::max(r.nck, 1)) return false;  // empty split
     // staged activations: VALU rows of lds_stride elements (padded by one
-    // chunk); MFMA one 1 KB operand fragment per 32-wide K step; MFMA_GA none
+    // chunk); MFMA one 1 KB operand fragment per 32-wide K step; the _GA
+    // variants none
     r.lds_stride = r.wg_chunks * kChunk + kChunk;
     size_t a_bytes = 0;
     if (cfg.inner == SKG_INNER_VALU)
@@ -246,17 +250,19 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
         a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
     // MFMA: one transpose tile per 16-row tile of B per wave, plus one for A (GA)
-    const int tiles = (cfg.inner == SKG_INNER_VALU)  ? 0
+    const int tiles = valu                            ? 0
                       : (cfg.inner == SKG_INNER_MFMA) ? cfg.row_tiles
                                                       : cfg.row_tiles + 1;
     const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
     r.stash_offset = (int)(r.tr_offset + tr_bytes);
     // stash: every wave's partial sums of each of the workgroup's row blocks
     // (VALU: M x its rows; MFMA: one 16 x 16 fp32 tile per 16 rows)
-    const size_t per_block = (cfg.inner == SKG_INNER_VALU) ? (size_t)M * r.rows_per_wg
-                                                           : (size_t)16 * r.rows_per_wg;
+    const size_t per_block = valu ? (size_t)M * r.rows_per_wg : (size_t)16 * r.rows_per_wg;
     const size_t blocks_per_wg = (size_t)ceil_div(r.num_rb, r.grid_rb);
-    const size_t stash_bytes = blocks_per_wg * cfg.waves_k * per_block * sizeof(float);
+    // (a row block covered by one wave is written from registers)
+    const bool direct = cfg.waves_k == 1 && cfg.backend != SKG_BACKEND_SPLITK;
+    const size_t stash_bytes =
+        direct ? 0 : blocks_per_wg * cfg.waves_k * per_block * sizeof(float);
     if (r.stash_offset + stash_bytes > (size_t)kMaxLdsBytes) return false;
     r.flag_offset = (int)(r.stash_offset + stash_bytes);
     r.lds_bytes = r.flag_offset + 16;

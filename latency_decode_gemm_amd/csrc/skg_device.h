@@ -306,33 +306,44 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
 }
 
 // ---- epilogue ------------------------------------------------------------------
-// After its stream, a workgroup holds in LDS (the stash) each wave's partial
-// sums of each of its row blocks.  Its threads then take the outputs of a row
-// block in (m, row) order, add the waves_k partials in wave order, and write
-// C (split_k == 1) or the split's partial (split_k > 1; the single-pass
-// backend then settles the row block with splitk_complete).  IDX maps (row
-// block b, K-wave q, token m, local row rl) to the stash index.
-template <class IDX>
+// A row block whose K range is covered by one wave is written straight from
+// that wave's registers.  Otherwise (waves_k > 1, or the single-pass split-K
+// backend, which settles row blocks workgroup by workgroup) each wave parks
+// its partial sums of each row block in LDS (the stash), and after the stream
+// the workgroup's threads take (token, local row) pairs, consecutive threads
+// consecutive rows, add the waves_k partials in wave order, and write C
+// (split_k == 1) or the split's partial (split_k > 1; the single-pass backend
+// then settles the row block with splitk_complete).  base(b, q, rl) is the
+// stash index of token 0 of (row block b, K-wave q, local row rl); mofs(m)
+// adds token m.
+__device__ __forceinline__ bool direct_write(const KParams &p) {
+    return p.waves_k == 1 && (p.split_k == 1 || p.two_pass);
+}
+
+template <class BASE, class MOFS>
 __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, const float *stash,
-                                             unsigned *flag, IDX idx) {
+                                             unsigned *flag, BASE base, MOFS mofs) {
     __syncthreads();
-    const int NB = p.rows_per_wg;
-    const int total = p.M * NB;
+    const int NB = p.rows_per_wg;  // never more than the workgroup's threads
+    const int M = p.M;
+    // thread -> local row rl and tokens m0, m0 + mstep, ...
+    const int m0 = threadIdx.x / NB;
+    const int rl = threadIdx.x - m0 * NB;
+    const int mstep = blockDim.x / NB;
     for (int b = 0; b < w.nblk; ++b) {
         const int rb = w.rb0 + b * w.rbs;
-        float *part = (p.split_k > 1) ? p.ws + (size_t)(rb * p.split_k + w.s) * total : nullptr;
-        for (int i = threadIdx.x; i < total; i += blockDim.x) {
-            const int m = i / NB;
-            const int rl = i - m * NB;
-            float v = stash[idx(b, 0, m, rl)];
-            for (int q = 1; q < p.waves_k; ++q) v += stash[idx(b, q, m, rl)];
+        const int row = rb * NB + rl;
+        float *part = (p.split_k > 1) ? p.ws + (size_t)(rb * p.split_k + w.s) * M * NB + rl
+                                      : nullptr;
+        for (int m = m0; m < M; m += mstep) {
+            float v = stash[base(b, 0, rl) + mofs(m)];
+            for (int q = 1; q < p.waves_k; ++q) v += stash[base(b, q, rl) + mofs(m)];
             if (p.split_k == 1) {
-                const int row = rb * NB + rl;
                 if (row < p.N) store_c(p, m, row, v);
             } else if (p.two_pass) {
-                part[i] = v;
+                part[m * NB] = v;
             } else {
-                ws_store(part + i, v);
+                ws_store(part + m * NB, v);
             }
         }
         if (p.split_k > 1 && !p.two_pass) {
@@ -342,10 +353,40 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
     }
 }
 
+// Barrier after staging A with direct-to-LDS loads that were issued before
+// the NV newest vector memory operations of this wave: waits for everything
+// older than those (vmcnt) and for this wave's LDS stores (lgkmcnt), then
+// meets the other waves.  A fence over LDS here would make the compiler wait
+// for every outstanding load (it cannot tell the staging loads from the
+// ring's), so only compiler-level fences keep LDS accesses on their side.
+template <int NV>
+__device__ __forceinline__ void staged_barrier();
+
+// s_waitcnt that waits until at most n vector memory operations of this wave
+// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int NV>
+__device__ __forceinline__ void staged_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vmcnt<NV>();
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- VALU kernel --------------------------------------------------------------
 // M: tokens (compile time); R: row slots per wave (4 rows each);
-// PF: K-steps of B loads in flight (register ring depth).
-template <int M, int R, int PF>
+// PF: K-steps of B loads in flight (register ring depth); AG: each step's
+// activation chunks are loaded from global memory (L2-resident) into the same
+// ring as B, instead of being staged in LDS before the stream (no staging
+// latency and no barrier; M more loads per step).
+template <int M, int R, int PF, bool AG>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
@@ -377,10 +418,14 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         for (int r = 0; r < R; ++r)
             rowp[r] = (b < w.nblk) ? p.B + (int64_t)min(rbase + 4 * r, p.N - 1) * p.ldb : p.A;
     };
-    auto issue = [&](uint4(&dst)[R]) {
+    constexpr int NA = AG ? M : 1;
+    auto issue = [&](uint4(&dst)[R], uint4(&adst)[NA]) {
         const int64_t off = window_off(wv_c0 + lst * kValuStep + l16, p);
 #pragma unroll
         for (int r = 0; r < R; ++r) dst[r] = ldg16_stream(rowp[r] + off);
+        if constexpr (AG)
+#pragma unroll
+            for (int m = 0; m < M; ++m) adst[m] = ldg16(p.A + (int64_t)m * p.lda + off);
         if (++lst == SPB) {
             lst = 0;
             set_rows(++lb);
@@ -388,12 +433,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     };
 
     uint4 buf[PF][R];
+    uint4 abuf[PF][NA];
     set_rows(0);
+    if constexpr (AG) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) issue(buf[i]);
-
-    stage_a(p, As, w.wg_c0);
-    __syncthreads();
+        for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
+    } else {
+        // A is staged first, so waiting for it (the oldest loads) leaves the
+        // ring's loads in flight
+        stage_a(p, As, w.wg_c0);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
+        staged_barrier<PF * R>();
+    }
 
     float acc[R][M];
 #pragma unroll
@@ -406,24 +458,34 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     const uint16_t *ap = As + (wk * p.wave_chunks + l16) * kChunk;
     // stash: [row block][K-wave][m][local row]
     const int per_block = p.waves_k * M * NB;
+    const bool direct = direct_write(p);
 
     int cb = 0, cst = 0;  // compute cursor
-    auto step = [&](uint4(&bv)[R]) {
+    auto step = [&](uint4(&bv)[R], uint4(&av)[NA]) {
         if (cst >= tail_st) {
             const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + l16, p);
 #pragma unroll
             for (int r = 0; r < R; ++r) bv[r] = and4(bv[r], mk);
-        }
-        const uint16_t *a_st = ap + cst * (kValuStep * kChunk);
-        uint4 a[M];
+            if constexpr (AG)
 #pragma unroll
-        for (int m = 0; m < M; ++m) a[m] = lds16(a_st + m * p.lds_stride);
+                for (int m = 0; m < M; ++m) av[m] = and4(av[m], mk);
+        }
+        uint4 a[M];
+        if constexpr (AG) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) a[m] = av[m];
+        } else {
+            const uint16_t *a_st = ap + cst * (kValuStep * kChunk);
+#pragma unroll
+            for (int m = 0; m < M; ++m) a[m] = lds16(a_st + m * p.lds_stride);
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m) acc[r][m] = dot8(a[m], bv[r], acc[r][m]);
         if (++cst == SPB) {
             // row block done: lane m of each row group now takes token m
+            const int rb = w.rb0 + cb * w.rbs;
             float *dst = stash + cb * per_block + (wk * M + l16) * NB + rl0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -431,7 +493,16 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 #pragma unroll
                 for (int j = 0; j < VP; ++j) v[j] = (j < M) ? acc[r][j] : 0.0f;
                 reduce16<VP>(v, lane);
-                if (writer) dst[4 * r] = v[0];
+                if (writer) {
+                    if (!direct) {
+                        dst[4 * r] = v[0];
+                    } else if (p.split_k == 1) {
+                        const int row = rb * NB + rl0 + 4 * r;
+                        if (row < p.N) store_c(p, l16, row, v[0]);
+                    } else {
+                        p.ws[((size_t)(rb * p.split_k + w.s) * M + l16) * NB + rl0 + 4 * r] = v[0];
+                    }
+                }
 #pragma unroll
                 for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
             }
@@ -448,13 +519,15 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     for (int t0 = 0; t0 < TT; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (t0 + i < T) step(buf[i]);
-            issue(buf[i]);
+            if (t0 + i < T) step(buf[i], abuf[i]);
+            issue(buf[i], abuf[i]);
         }
     }
-    write_blocks(p, w, stash, flag, [&](int b, int q, int m, int rl) {
-        return (b * p.waves_k + q) * M * NB + m * NB + rl;
-    });
+    if (!direct)
+        write_blocks(
+            p, w, stash, flag,
+            [&](int b, int q, int rl) { return (b * p.waves_k + q) * M * NB + rl; },
+            [&](int m) { return m * NB; });
 }
 
 // ---- MFMA kernel ------------------------------------------------------------
@@ -562,12 +635,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     uint4 buf[PF][G][4];
     uint4 abuf[PF][NA];
     set_rows(0);
+    if constexpr (!AG) stage_a_frag(p, As, w.wg_c0);  // oldest loads, as in the VALU kernel
 #pragma unroll
     for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
 
     if constexpr (!AG) {
-        stage_a_frag(p, As, w.wg_c0);
-        __syncthreads();
+        staged_barrier<PF * G * 4>();
     } else {
         // activation rows 4 * AQ .. 15 of the A tile stay zero
 #pragma unroll
@@ -587,6 +660,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     // lane 16*hi + lo, element v holds token 4*hi + v, row 16*tile + lo
     f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * 64 + lane;
     const int st_block = p.waves_k * p.waves_n * G * 64;  // f32x4 per row block
+    const bool direct = direct_write(p);
+    const int rlw = wn * (16 * G);  // first local row of this wave
 
     int cb = 0, cst = 0;
     auto step = [&](uint4(&bv)[G][4], uint4(&av)[NA]) {
@@ -630,9 +705,26 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             }
         }
         if (++cst == SPB) {
+            // acc[t][v] holds token 4*hi + v of local row rlw + 16*t + lo
+            const int rb = w.rb0 + cb * w.rbs;
 #pragma unroll
             for (int t = 0; t < G; ++t) {
-                st[cb * st_block + t * 64] = acc[t];
+                if (!direct) {
+                    st[cb * st_block + t * 64] = acc[t];
+                } else {
+                    const int rl = rlw + 16 * t + lo;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = 4 * hi + v;
+                        if (m < M) {
+                            if (p.split_k == 1) {
+                                if (rb * NB + rl < p.N) store_c(p, m, rb * NB + rl, acc[t][v]);
+                            } else {
+                                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
+                            }
+                        }
+                    }
+                }
                 acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
             cst = 0;
@@ -649,19 +741,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             issue(buf[i], abuf[i]);
         }
     }
-    write_blocks(p, w, stash, flag, [&](int b, int q, int m, int rl) {
-        const int wq = rl / (16 * G);     // N-wave
-        const int t = (rl >> 4) % G;      // tile
-        const int l = 16 * (m >> 2) + (rl & 15);
-        return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + l * 4 + (m & 3);
-    });
+    if (!direct)
+        write_blocks(
+            p, w, stash, flag,
+            [&](int b, int q, int rl) {
+                const int wq = rl / (16 * G);  // N-wave
+                const int t = (rl >> 4) % G;   // tile
+                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + (rl & 15) * 4;
+            },
+            [&](int m) { return 64 * (m >> 2) + (m & 3); });
 }
 
 // Instantiation list for one M, in the order of kValuVariants.
-#define SKG_VALU_ROW(M)                                                             \
-    {skg_valu_kernel<M, 1, 4>, skg_valu_kernel<M, 1, 8>, skg_valu_kernel<M, 1, 12>,  \
-     skg_valu_kernel<M, 2, 2>, skg_valu_kernel<M, 2, 4>, skg_valu_kernel<M, 2, 8>,   \
-     skg_valu_kernel<M, 4, 2>, skg_valu_kernel<M, 4, 4>}
+#define SKG_VALU_ROW(M, AG)                                                              \
+    {skg_valu_kernel<M, 1, 4, AG>, skg_valu_kernel<M, 1, 8, AG>,                         \
+     skg_valu_kernel<M, 1, 12, AG>, skg_valu_kernel<M, 2, 2, AG>,                        \
+     skg_valu_kernel<M, 2, 4, AG>, skg_valu_kernel<M, 2, 8, AG>,                         \
+     skg_valu_kernel<M, 4, 2, AG>, skg_valu_kernel<M, 4, 4, AG>}
 
 }  // namespace
 }  // namespace skg

@@ -89,13 +89,15 @@ hipError_t probe_kernels();
 constexpr int kTileBytes = 4096;
 
 // Kernel variants.  VALU (row_tiles R, depth PF) pairs, in table order; the
-// instantiations live in skg_valu_lo.hip (M = 1..8) and skg_valu_hi.hip
-// (M = 9..16), the MFMA ones in skg_launch.hip.
+// instantiations live in skg_valu_lo.hip (M = 1..8), skg_valu_hi.hip
+// (M = 9..16) and skg_valu_ga.hip (activations from global memory, M = 1..8),
+// the MFMA ones in skg_launch.hip.
 using KernelPtr = void (*)(KParams);
 constexpr int kValuVariants[][2] = {{1, 4}, {1, 8}, {1, 12}, {2, 2},
                                      {2, 4}, {2, 8}, {4, 2}, {4, 4}};
 constexpr int kNumValu = sizeof(kValuVariants) / sizeof(kValuVariants[0]);
 KernelPtr valu_kernel_lo(int M, int variant);
 KernelPtr valu_kernel_hi(int M, int variant);
+KernelPtr valu_kernel_ga(int M, int variant);  // activations from global memory, M <= 8
 
 }  // namespace skg

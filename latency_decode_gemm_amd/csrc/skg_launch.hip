@@ -80,10 +80,12 @@ const MfmaVariant kMfmaVariants[] = {SKG_MFMA(1, 2), SKG_MFMA(1, 3), SKG_MFMA(1,
 constexpr int kNumMfma = sizeof(kMfmaVariants) / sizeof(kMfmaVariants[0]);
 
 KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
-    if (inner == SKG_INNER_VALU) {
+    if (inner == SKG_INNER_VALU || inner == SKG_INNER_VALU_GA) {
         for (int i = 0; i < kNumValu; ++i)
-            if (kValuVariants[i][0] == row_tiles && kValuVariants[i][1] == depth)
+            if (kValuVariants[i][0] == row_tiles && kValuVariants[i][1] == depth) {
+                if (inner == SKG_INNER_VALU_GA) return M <= 8 ? valu_kernel_ga(M, i) : nullptr;
                 return M <= 8 ? valu_kernel_lo(M, i) : valu_kernel_hi(M, i);
+            }
         return nullptr;
     }
     if (inner == SKG_INNER_MFMA || inner == SKG_INNER_MFMA_GA) {

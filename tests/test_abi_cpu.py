@@ -95,10 +95,17 @@ def test_check_config_rules():
     assert not skg.skinny_gemm_check_config(16, 7168, 256, big)
     assert skg.skinny_gemm_check_config(16, 7168, 256, mk(inner=skg.SKG_INNER_MFMA, split_k=2,
                                                           row_tiles=1, waves_k=4, depth=4))
+    # activations in the load ring: M <= 8 and M * depth <= 32
+    ga = dict(inner=skg.SKG_INNER_VALU_GA, split_k=1, row_tiles=1, waves_k=4)
+    assert skg.skinny_gemm_check_config(8, 7168, 256, mk(depth=4, **ga))
+    assert not skg.skinny_gemm_check_config(9, 7168, 256, mk(depth=4, **ga))
+    assert not skg.skinny_gemm_check_config(8, 7168, 256, mk(depth=8, **ga))
+    assert skg.skinny_gemm_check_config(2, 7168, 256, mk(depth=12, **ga))
 
 
 def test_compiled_variant_lists_match_library():
     for inner, allowed in ((skg.SKG_INNER_VALU, _capi.VALU_VARIANTS),
+                           (skg.SKG_INNER_VALU_GA, [v for v in _capi.VALU_VARIANTS if 4 * v[1] <= 32]),
                            (skg.SKG_INNER_MFMA, _capi.MFMA_VARIANTS),
                            (skg.SKG_INNER_MFMA_GA, _capi.MFMA_VARIANTS)):
         for rt in (1, 2, 3, 4, 8):

@@ -44,16 +44,21 @@ def test_default_equals_explicit_dispatch_config():
 
 def test_split_k_forced_is_reproducible():
     torch = gu.torch_cuda()
-    A, B = _problem(16, 7168, 256)
-    for cfg in (MK(inner=skg.SKG_INNER_MFMA, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=2),
-                MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=skg.SKG_INNER_MFMA_GA, split_k=4,
-                   row_tiles=1, waves_n=1, waves_k=2, depth=2),
-                MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2, depth=4)):
+    cases = [(16, MK(inner=skg.SKG_INNER_MFMA, split_k=4, row_tiles=1, waves_n=1, waves_k=2,
+                     depth=2)),
+             (16, MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=skg.SKG_INNER_MFMA_GA, split_k=4,
+                     row_tiles=1, waves_n=1, waves_k=2, depth=2)),
+             (16, MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2,
+                     depth=4)),
+             (8, MK(inner=skg.SKG_INNER_VALU_GA, split_k=3, row_tiles=2, waves_n=1, waves_k=2,
+                    depth=2))]
+    for M, cfg in cases:
+        A, B = _problem(M, 7168, 256)
         ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))
         for _ in range(100):
             c = skg.skinny_gemm_bf16_with_config(A, B, cfg)
         torch.cuda.synchronize()
-        assert np.array_equal(gu.bits_of(c), ref)
+        assert np.array_equal(gu.bits_of(c), ref), (M, cfg)
 
 
 def test_warmup_then_same_bits():

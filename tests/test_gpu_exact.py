@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
 
 MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
+VG = skg.SKG_INNER_VALU_GA
 
 FAMILIES = [
     None,  # the dispatch table's choice
@@ -31,13 +32,23 @@ FAMILIES = [
        waves_k=2, depth=2),
     MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=V, split_k=2, row_tiles=2, waves_n=1,
        waves_k=2, depth=4),
+    MK(inner=VG, split_k=1, row_tiles=1, waves_n=1, waves_k=1, depth=4),
+    MK(inner=VG, split_k=1, row_tiles=2, waves_n=2, waves_k=4, depth=4),
+    MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=VG, split_k=3, row_tiles=4, waves_n=1,
+       waves_k=2, depth=2),
 ]
+
+
+def _m_for(cfg, m):
+    """Tokens for a test shape: the activation-ring VALU kernel takes M <= 8."""
+    return min(m, 8) if cfg is not None and cfg.inner == VG else m
 
 
 def _fid(c):
     if c is None:
         return "dispatch"
-    return ("p2_" if c.backend == 2 else "") + {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
+    return ("p2_" if c.backend == 2 else "") + \
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
 
 
@@ -84,7 +95,7 @@ def test_identity(cfg):
     torch = gu.torch_cuda()
     rng = np.random.default_rng(8)
     K = N = 256
-    M = 16
+    M = _m_for(cfg, 16)
     A_bits = _dyadic(rng, (M, K), -127, 127, 2.0 ** -3)
     B_bits = np.zeros((N, K), dtype=np.uint16)
     B_bits[np.arange(K), np.arange(K)] = 0x3F80
@@ -120,7 +131,7 @@ def test_bf16_rounding_is_nearest_even(cfg):
     exact value (the oracle's rounding), bit for bit; ties included."""
     torch = gu.torch_cuda()
     rng = np.random.default_rng(9)
-    M, K, N = 16, 48, 96
+    M, K, N = _m_for(cfg, 16), 48, 96
     A_bits = _dyadic(rng, (M, K), -16, 16, 1.0)
     B_bits = _dyadic(rng, (N, K), -255, 255, 2.0 ** -8)
     # hand-made ties in the first columns: 1 + 2^-8 -> 1.0, 1 + 3*2^-8 -> 1 + 2^-6

@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
+VG = skg.SKG_INNER_VALU_GA
 P2 = skg.SKG_BACKEND_SPLITK_2PASS
 
 
@@ -56,7 +57,11 @@ def _configs():
         out += [MK(inner=V, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
                 MK(inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF, rb_per_wg=3),
                 MK(inner=V, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
-                MK(backend=P2, inner=V, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF)]
+                MK(backend=P2, inner=V, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF),
+                MK(inner=VG, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
+                MK(inner=VG, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF, rb_per_wg=3),
+                MK(inner=VG, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
+                MK(backend=P2, inner=VG, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF)]
     for (G, PF) in skg._capi.MFMA_VARIANTS:
         out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 # 8 waves of 4 transpose tiles each would not leave LDS for A
@@ -76,7 +81,8 @@ SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 7
 
 
 def _cfg_id(c):
-    return ("p2_" if c.backend == P2 else "") + {V: "valu", F: "mfma", GA: "mfmaga"}[c.inner] + \
+    return ("p2_" if c.backend == P2 else "") + \
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_d{c.depth}_b{c.rb_per_wg}"
 
 
