@@ -513,16 +513,20 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 
     // Whole rounds of the ring: every slot is refilled unconditionally right
     // after it is consumed, so the compiler keeps each slot in the same
-    // registers and waits for exactly that slot's loads.  Steps past T only
-    // refill (from A, see set_rows).
+    // registers and waits for exactly that slot's loads.  The last round only
+    // consumes; refills for steps past T read A (see set_rows).
     const int TT = (T + PF - 1) / PF * PF;
-    for (int t0 = 0; t0 < TT; t0 += PF) {
+    int t0 = 0;
+    for (; t0 + PF < TT; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             if (t0 + i < T) step(buf[i], abuf[i]);
             issue(buf[i], abuf[i]);
         }
     }
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+        if (t0 + i < T) step(buf[i], abuf[i]);
     if (!direct)
         write_blocks(
             p, w, stash, flag,
@@ -712,10 +716,14 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                 if (!direct) {
                     st[cb * st_block + t * 64] = acc[t];
                 } else {
-                    const int rl = rlw + 16 * t + lo;
+                    // lane index re-derived here so the compiler cannot keep
+                    // the store addresses live across the whole stream
+                    int ln = lane;
+                    __asm__ volatile("" : "+v"(ln));
+                    const int rl = rlw + 16 * t + (ln & 15);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * hi + v;
+                        const int m = 4 * (ln >> 4) + v;
                         if (m < M) {
                             if (p.split_k == 1) {
                                 if (rb * NB + rl < p.N) store_c(p, m, rb * NB + rl, acc[t][v]);
@@ -732,7 +740,9 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
         }
     };
 
-    // whole rounds of the ring, as in the VALU kernel
+    // Whole rounds of the ring, as in the VALU kernel, but the last round
+    // refills too (from A): a separate last round costs this kernel more
+    // registers than the few extra cache-resident loads cost time.
     const int TT = (T + PF - 1) / PF * PF;
     for (int t0 = 0; t0 < TT; t0 += PF) {
 #pragma unroll
