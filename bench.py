@@ -41,7 +41,7 @@ ROTATE_BYTES = 1 << 30  # footprint between two uses of one weight copy
 DEFAULT_WORKLOAD = "wide_deep"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
-                  "skg_valu_hi.hip", "skg_api.cpp", "tuned_table.inc"]
+                  "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_api.cpp", "tuned_table.inc"]
 
 
 def kernel_source_hash() -> str:
