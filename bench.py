@@ -18,8 +18,14 @@ Prints ONE JSON line:
                  its dispatches record (skinny_gemm_bf16_timed) on every step
                  of the timed region;
   cpu_baseline = the CPU oracle timed on this host over the same workload.
-``--points-out`` also writes per-point microseconds per call for every
-workload point (eager launches and HIP-graph replay) as JSON.
+``--points-out FILE`` also writes, for every one of the 29 workload points,
+the kernel time per call (median of 200 dispatch-recorded event pairs), the
+time per call eager, from HIP-graph replay and with one hot weight copy, the
+streaming-read ceiling for the same weight bytes, and the CPU oracle on all
+host cores and on one core (the CPU-baseline leg per point).  A K = 0 call
+(the zero-fill kernel) precedes each point's dispatches, so that a rocprofv3
+kernel trace of the run can be split by point:
+``python -m latency_decode_gemm_amd.trace_points TRACE.csv FILE``.
 """
 from __future__ import annotations
 
@@ -209,6 +215,101 @@ def cpu_baseline(oracle, pts, bpool, budget_s):
                       f"{t_total:.1f} s; binary64 C loop, OpenMP over columns"}
 
 
+def oracle_mod():
+    import oracle
+    return oracle
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=20):
+    """Every workload point: kernel time per call from the dispatches' own
+    events (median of `calls`), HIP-graph and eager time per call, the same
+    with one hot weight copy, the streaming-read ceiling for the weight size,
+    and the CPU oracle on all host cores and on one core (median of 3 after a
+    warm-up).  Each point's timed dispatches follow one K = 0 call (the
+    zero-fill kernel) that marks them in a kernel trace, so a rocprofv3
+    kernel trace of this run can be attributed to points by order."""
+    h = stream.cuda_stream
+    spec = inputs.all_points()
+    shapes = list(dict.fromkeys((p["K"], p["N"]) for p in spec))
+    table = {}
+    order = 0
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+    for (K, N) in shapes:
+        sub = [p for p in spec if (p["K"], p["N"]) == (K, N)]
+        bp = BPool(torch, inputs, [(K, N)])
+        ps = [Point(torch, skg, inputs, p, bp) for p in sub]
+        skg.skinny_gemm_warmup([(K, N)], [p.M for p in ps], stream=stream)
+        ev = [(skg.HipEvent(), skg.HipEvent()) for _ in range(calls)]
+        for pt in ps:
+            st = lib.skinny_gemm_bf16(pt.A.data_ptr(), pt.A.data_ptr(), pt.Cbuf.data_ptr(), pt.M,
+                                      pt.N, 0, 8, 8, pt.ldc, pt.odt, h)  # trace marker (K = 0)
+            if st != 0:
+                raise RuntimeError(f"marker call failed: status {st}")
+            for _ in range(warm):
+                call(lib, pt, next_copy(pt), h)
+            for i in range(calls):
+                call(lib, pt, next_copy(pt), h, ev[i])
+            torch.cuda.synchronize()
+            ev_us = [a.elapsed_ms(b) * 1000.0 for a, b in ev]
+            table[pt.name()] = {
+                "M": pt.M, "K": pt.K, "N": pt.N, "out": pt.out, "ldc": pt.ldc,
+                "config": pt.cfg.as_dict(), "trace_order": order, "trace_warm": warm,
+                "trace_calls": calls,
+                "dispatches_per_call": 2 if pt.cfg.backend == skg.SKG_BACKEND_SPLITK_2PASS else 1,
+                "kernel_us_events_median": round(median(ev_us), 3),
+                "weight_bytes": pt.weight_bytes, "alg_bytes": pt.alg_bytes}
+            order += 1
+        eager = time_points_eager(torch, lib, ps, stream)
+        graph = time_points_graph(torch, lib, ps, stream)
+        # streaming-read ceiling over the same rotating weight copies
+        lst = bp[(K, N)]["list"]
+        nb = 2 * N * K
+        for i in range(4):
+            lib.skinny_gemm_stream_read(lst[i % len(lst)].data_ptr(), nb, sink.data_ptr(), h)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            for i in range(calls):
+                lib.skinny_gemm_stream_read(lst[i % len(lst)].data_ptr(), nb, sink.data_ptr(), h)
+            e1.record()
+        torch.cuda.synchronize()
+        read_us = e0.elapsed_time(e1) * 1000.0 / calls
+        hot = BPool(torch, inputs, [(K, N)], rotate_bytes=0)
+        for p in ps:
+            p.copies = hot[(K, N)]
+            p.copies["list"] = p.copies["list"][:1]
+        hot_us = time_points_graph(torch, lib, ps, stream)
+        for pt in ps:
+            e = table[pt.name()]
+            e.update({"us_per_call_eager": round(eager[pt.name()], 3),
+                      "us_per_call_graph": round(graph[pt.name()], 3),
+                      "us_per_call_hot_graph": round(hot_us[pt.name()], 3),
+                      "read_ceiling_us_eager": round(read_us, 3)})
+            k_us = e["kernel_us_events_median"]
+            e["weight_GBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3, 1)
+            e["frac_of_8TBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3 / PEAK_HBM_GBS, 4)
+            # CPU oracle on this point
+            bits_B = bp.bits[(K, N)]
+            for threads, key in ((oracle.default_threads(), "cpu_all_cores"), (1, "cpu_one_core")):
+                ts = []
+                for rep in range(4):
+                    t0 = time.perf_counter()
+                    oracle.gemm_f64(pt.A_bits, bits_B, K, threads=threads)
+                    ts.append(time.perf_counter() - t0)
+                e[key] = {"us_per_call": round(median(ts[1:]) * 1e6, 1), "threads": threads}
+        del ps, bp, hot
+        torch.cuda.empty_cache()
+        print(f"points: K={K} N={N} done", file=sys.stderr, flush=True)
+    return table
+
+
 def load_traffic(dominant_name):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -341,34 +442,9 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.points_out:
-        all_pts_spec = inputs.all_points()
-        shapes_all = list(dict.fromkeys((p["K"], p["N"]) for p in all_pts_spec))
         del pts, bpool
         torch.cuda.empty_cache()
-        table = {}
-        for (K, N) in shapes_all:
-            sub = [p for p in all_pts_spec if (p["K"], p["N"]) == (K, N)]
-            bp = BPool(torch, inputs, [(K, N)])
-            ps = [Point(torch, skg, inputs, p, bp) for p in sub]
-            skg.skinny_gemm_warmup([(K, N)], [p.M for p in ps], stream=stream)
-            eager = time_points_eager(torch, lib, ps, stream)
-            graph = time_points_graph(torch, lib, ps, stream)
-            hot = BPool(torch, inputs, [(K, N)], rotate_bytes=0)
-            for p in ps:
-                p.copies = hot[(K, N)]
-                p.copies["list"] = p.copies["list"][:1]
-            hot_us = time_points_graph(torch, lib, ps, stream)
-            for p in ps:
-                nm = p.name()
-                table[nm] = {"M": p.M, "K": p.K, "N": p.N, "out": p.out, "ldc": p.ldc,
-                             "config": p.cfg.as_dict(),
-                             "us_per_call_eager": round(eager[nm], 3),
-                             "us_per_call_graph": round(graph[nm], 3),
-                             "weight_GBps_graph": round(p.weight_bytes / graph[nm] / 1e3, 1),
-                             "frac_of_8TBps_graph": round(p.weight_bytes / graph[nm] / 1e3 / PEAK_HBM_GBS, 4),
-                             "us_per_call_hot_graph": round(hot_us[nm], 3)}
-            del ps, bp, hot
-            torch.cuda.empty_cache()
+        table = points_report(torch, np, skg, lib, inputs, oracle_mod(), stream)
         with open(args.points_out, "w") as f:
             json.dump(table, f, indent=1)
     print(json.dumps(line), flush=True)

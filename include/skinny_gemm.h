@@ -179,6 +179,17 @@ int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values,
 /* 1 if a gfx950 device is current and the library's kernels load, else 0. */
 int skinny_gemm_available(void);
 
+/* Measurement aid, not part of the GEMM: streams `bytes` bytes from the
+   device buffer `src` with the GEMM's own load form (128-bit non-temporal
+   loads; 512 workgroups of 256 threads, 8 loads per thread in flight per
+   round) and folds them (XOR of 32-bit words) into `sink`, one 32-bit word
+   per workgroup (device memory, at least 2048 bytes, caller-owned).  The XOR
+   of the 512 words equals the XOR of all 32-bit words of the buffer.  The
+   duration of this kernel is the streaming-read ceiling the GEMM's
+   bandwidth figures are compared with.  `src` 16-byte aligned and `bytes` a
+   multiple of 16 (else SKG_ERR_MISALIGNED); bytes == 0 is a no-op. */
+int skinny_gemm_stream_read(const void *src, size_t bytes, void *sink, void *stream);
+
 /* Static description of a status code. */
 const char *skinny_gemm_strerror(int status);
 

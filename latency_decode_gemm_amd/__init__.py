@@ -11,7 +11,8 @@ from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_SPLITK, SKG_BACKEND_SPLITK_2PAS
                     SKG_OUT_BF16, SKG_OUT_F32, HipEvent, SkgConfig, SkinnyGemmError)
 from .ops import (skinny_gemm_available, skinny_gemm_bf16, skinny_gemm_bf16_timed,
                   skinny_gemm_bf16_with_config,
-                  skinny_gemm_check_config, skinny_gemm_dispatch, skinny_gemm_strerror,
+                  skinny_gemm_check_config, skinny_gemm_dispatch, skinny_gemm_stream_read,
+                  skinny_gemm_strerror,
                   skinny_gemm_warmup, skinny_gemm_warmup_keys, skinny_gemm_workspace_bytes)
 
 __all__ = [n for n in dir() if n.startswith(("skinny_gemm", "SKG_", "Skg", "Skinny", "Hip"))]

@@ -91,6 +91,7 @@ SIGNATURES = {
     "skinny_gemm_warmup_keys": (_i, [_ip, _i, _ip, _i, _cfgp, _i, _ip]),
     "skinny_gemm_warmup": (_i, [_ip, _i, _ip, _i, _vp, _ip]),
     "skinny_gemm_available": (_i, []),
+    "skinny_gemm_stream_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
     "skinny_gemm_strerror": (ctypes.c_char_p, [_i]),
 }
 

@@ -452,6 +452,17 @@ int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values, i
     return rc;
 }
 
+int skinny_gemm_stream_read(const void *src, size_t bytes, void *sink, void *stream) {
+    if (bytes == 0) return SKG_OK;
+    if (src == nullptr || sink == nullptr) return SKG_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) || (bytes & 15u)) return SKG_ERR_MISALIGNED;
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return SKG_ERR_MISALIGNED;
+    return launch_stream_read(src, bytes / 16, sink, reinterpret_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? SKG_OK
+               : SKG_ERR_HIP;
+}
+
 int skinny_gemm_available(void) {
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return 0;

@@ -82,6 +82,10 @@ hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
 hipError_t launch_small_k(const KParams &p, hipStream_t stream, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
 
+// Streaming-read probe: 512 x 256 threads fold `n16` 16-byte words into sink[512].
+constexpr int kReadProbeGrid = 512;
+hipError_t launch_stream_read(const void *src, size_t n16, void *sink, hipStream_t stream);
+
 // Loads a kernel's code object (forces lazy loading) for availability checks.
 hipError_t probe_kernels();
 

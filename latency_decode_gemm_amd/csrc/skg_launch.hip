@@ -41,6 +41,33 @@ __global__ void skg_small_k_kernel(KParams p) {
     }
 }
 
+// Streaming read with the GEMM's load form (non-temporal 128-bit loads); each
+// workgroup covers 8 x 4 KB contiguous per round and XOR-folds its words.
+__global__ void __launch_bounds__(256) skg_stream_read_kernel(const uint16_t *src, size_t n16,
+                                                              unsigned *sink) {
+    __shared__ unsigned red[256];
+    unsigned acc = 0;
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 8;
+    for (size_t base = (size_t)blockIdx.x * blockDim.x * 8 + threadIdx.x; base < n16;
+         base += stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t i = base + (size_t)u * blockDim.x;
+            v[u] = (i < n16) ? ldg16_stream(src + i * kChunk) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
 // Second pass of SKG_BACKEND_SPLITK_2PASS: C[m][row] = sum over s (in split
 // order) of ws[((rb*S + s)*M + m)*NB + rl]; consecutive threads take
 // consecutive rows, so partial reads and C writes are coalesced.
@@ -168,6 +195,13 @@ hipError_t launch_small_k(const KParams &p, hipStream_t stream, hipEvent_t start
                                   dim3(blocks), dim3(256), args, 0, stream, start, stop, 0);
     }
     hipLaunchKernelGGL(skg_small_k_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void *src, size_t n16, void *sink, hipStream_t stream) {
+    hipLaunchKernelGGL(skg_stream_read_kernel, dim3(kReadProbeGrid), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t *>(src), n16,
+                       reinterpret_cast<unsigned *>(sink));
     return hipGetLastError();
 }
 

@@ -155,6 +155,21 @@ def skinny_gemm_warmup(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int
     return int(n.value)
 
 
+def skinny_gemm_stream_read(src, sink, nbytes: Optional[int] = None, stream=None):
+    """Streams ``nbytes`` (default: all) bytes of the device tensor ``src``
+    through the GEMM's load form and XOR-folds them into ``sink`` (an int32
+    device tensor of >= 512 elements, one word per workgroup): the measured
+    streaming-read ceiling."""
+    torch = _torch()
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if not (src.is_cuda and sink.is_cuda) or sink.dtype != torch.int32 or sink.numel() < 512:
+        raise ValueError("src and sink must be device tensors, sink int32 with >= 512 elements")
+    check(_capi.lib().skinny_gemm_stream_read(src.data_ptr(), n, sink.data_ptr(),
+                                              _stream_handle(stream, src.device)),
+          "skinny_gemm_stream_read")
+    return sink
+
+
 def skinny_gemm_available() -> bool:
     return bool(_capi.lib().skinny_gemm_available())
 

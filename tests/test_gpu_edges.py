@@ -185,3 +185,28 @@ def test_error_returns():
     assert e.value.status == skg.SKG_ERR_MISALIGNED
     with pytest.raises(TypeError):
         skg.skinny_gemm_bf16(A9.float(), B9)
+
+
+def test_stream_read_probe_folds_every_word():
+    """The read-ceiling probe touches every 16-byte word exactly once: the XOR
+    of its per-workgroup words equals the XOR of the buffer; bad arguments are
+    rejected before any launch."""
+    torch = gu.torch_cuda()
+    rng = np.random.default_rng(11)
+    for nbytes in (16, 4096 + 48, (1 << 20) + 16 * 37, 3 << 22):
+        host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+        src = torch.from_numpy(host.view(np.int32)).cuda()
+        sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+        skg.skinny_gemm_stream_read(src, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), nbytes
+    lib = skg._capi.lib()
+    src = torch.zeros(64, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+    assert lib.skinny_gemm_stream_read(src.data_ptr() + 4, 16, sink.data_ptr(), None) == \
+        skg.SKG_ERR_MISALIGNED
+    assert lib.skinny_gemm_stream_read(src.data_ptr(), 24, sink.data_ptr(), None) == \
+        skg.SKG_ERR_MISALIGNED
+    assert lib.skinny_gemm_stream_read(src.data_ptr(), 16, None, None) == skg.SKG_ERR_INVALID_ARG
+    assert lib.skinny_gemm_stream_read(None, 0, None, None) == skg.SKG_OK
