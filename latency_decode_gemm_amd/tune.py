@@ -26,7 +26,8 @@ ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
 
 from latency_decode_gemm_amd._capi import MFMA_VARIANTS, VALU_VARIANTS
-WAVES = [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2), (1, 4), (2, 4), (1, 8)]
+WAVES = [(1, 1), (2, 1), (3, 1), (4, 1), (6, 1), (8, 1), (1, 2), (2, 2), (3, 2), (4, 2),
+         (1, 4), (2, 4), (1, 8)]
 SPLITS = [1, 2, 3, 4, 6, 8, 12, 16]
 GRID_TARGETS = [256, 512, 1024, 2048]
 
@@ -49,8 +50,11 @@ def structures(skg, M, K, N, inner_set):
                 for S in SPLITS:
                     grids = set()
                     for tgt in GRID_TARGETS:
-                        rpw = max(1, round(num_rb * S / tgt))
-                        grids.add(rpw)
+                        # nearest, and the fewest row blocks per workgroup
+                        # that keep the grid within the target (no CU gets a
+                        # second workgroup when the target is the CU count)
+                        grids.add(max(1, round(num_rb * S / tgt)))
+                        grids.add(max(1, math.ceil(num_rb * S / tgt)))
                     for rpw in sorted(grids):
                         grid = math.ceil(num_rb / rpw) * S
                         if grid < 32 or grid > 16384:
