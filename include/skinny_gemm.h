@@ -80,10 +80,16 @@ typedef enum {
     SKG_INNER_MFMA_GA = 2, /* as SKG_INNER_MFMA, with the activation fragments
                               read from global memory (L2) each K step: no LDS
                               for A, so any K fits in one workgroup */
-    SKG_INNER_VALU_GA = 3  /* as SKG_INNER_VALU, with each K step's activation
+    SKG_INNER_VALU_GA = 3, /* as SKG_INNER_VALU, with each K step's activation
                               chunks read from global memory (L2) into the
                               load ring: no staging, no LDS for A; M <= 8
                               and M * depth <= 32 */
+    SKG_INNER_MFMA_RING = 4,    /* as SKG_INNER_MFMA, with the weight loads
+                                   written straight into LDS tiles (a ring of
+                                   depth K steps per wave) instead of registers */
+    SKG_INNER_MFMA_RING_GA = 5  /* as SKG_INNER_MFMA_GA, with weights and
+                                   activation fragments both loaded straight
+                                   into the LDS ring */
 } skg_inner;
 
 #define SKG_MAX_M 16

@@ -30,6 +30,8 @@ SKG_INNER_VALU = 0
 SKG_INNER_MFMA = 1
 SKG_INNER_MFMA_GA = 2
 SKG_INNER_VALU_GA = 3
+SKG_INNER_MFMA_RING = 4
+SKG_INNER_MFMA_RING_GA = 5
 SKG_MAX_M = 16
 
 # Compiled (row_tiles, depth) pairs per inner product (the library's tables).

@@ -217,9 +217,9 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     } else {
         return false;
     }
-    if (cfg.inner != SKG_INNER_VALU && cfg.inner != SKG_INNER_MFMA &&
-        cfg.inner != SKG_INNER_MFMA_GA && cfg.inner != SKG_INNER_VALU_GA)
-        return false;
+    if (cfg.inner < SKG_INNER_VALU || cfg.inner > SKG_INNER_MFMA_RING_GA) return false;
+    const bool ring = cfg.inner == SKG_INNER_MFMA_RING || cfg.inner == SKG_INNER_MFMA_RING_GA;
+    const bool lds_frag = cfg.inner == SKG_INNER_MFMA || cfg.inner == SKG_INNER_MFMA_RING;
     const bool valu = cfg.inner == SKG_INNER_VALU || cfg.inner == SKG_INNER_VALU_GA;
     // VALU_GA keeps depth x M activation chunks in registers
     if (cfg.inner == SKG_INNER_VALU_GA && (M > 8 || M * cfg.depth > 32)) return false;
@@ -246,13 +246,13 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     size_t a_bytes = 0;
     if (cfg.inner == SKG_INNER_VALU)
         a_bytes = (size_t)M * r.lds_stride * 2;
-    else if (cfg.inner == SKG_INNER_MFMA)
+    else if (lds_frag)
         a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
     // MFMA: one transpose tile per 16-row tile of B per wave, plus one for A (GA)
-    const int tiles = valu                            ? 0
-                      : (cfg.inner == SKG_INNER_MFMA) ? cfg.row_tiles
-                                                      : cfg.row_tiles + 1;
+    // (the LDS ring: depth slots of those tiles)
+    const int tiles = (valu ? 0 : lds_frag ? cfg.row_tiles : cfg.row_tiles + 1) *
+                      (ring ? cfg.depth : 1);
     const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
     r.stash_offset = (int)(r.tr_offset + tr_bytes);
     // stash: every wave's partial sums of each of the workgroup's row blocks

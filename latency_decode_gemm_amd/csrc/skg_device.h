@@ -80,6 +80,31 @@ __device__ __forceinline__ void lds_dma16(const uint16_t *gsrc, void *lds_base) 
     __builtin_amdgcn_global_load_lds((gptr_t)(gsrc), (lptr_t)(lds_base), 16, 0, 0);
 }
 
+// The same as an instruction the compiler does not see into: its wait
+// insertion would otherwise drain every load before any LDS read that may
+// alias such a write (so a ring of them would never have more than one step
+// in flight).  The caller waits for the data itself (wait_vmcnt).  lds_addr
+// is the wave-uniform LDS byte address of lane 0's 16 bytes; NT marks the
+// load non-temporal (weights, read once).
+__device__ __forceinline__ uint32_t lds_addr_of(const void *lds_ptr) {
+    typedef __attribute__((address_space(3))) const void *lptr_t;
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lptr_t)(lds_ptr));
+}
+template <bool NT>
+__device__ __forceinline__ void lds_dma16_raw(const uint16_t *gsrc, uint32_t lds_addr) {
+    if constexpr (NT)
+        __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                         :
+                         : "v"(gsrc), "s"(lds_addr)
+                         : "memory", "m0");
+    else
+        __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(gsrc), "s"(lds_addr)
+                         : "memory", "m0");
+}
+
 // Workgroup barrier that orders LDS accesses only: outstanding global loads
 // stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -541,6 +566,9 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 // ds_read_b128.  One direct-to-LDS load per step block; tokens m >= M load
 // row M-1 (the readers mask them to zero); chunks at or beyond K are written
 // as (partial) zeros by ordinary LDS stores.
+// (RAW: through lds_dma16_raw, for kernels whose other LDS writes by DMA the
+// compiler does not see either; their barrier waits for these loads)
+template <bool RAW = false>
 __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int wg_c0) {
     const int lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
@@ -550,10 +578,14 @@ __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int
     for (int blk = threadIdx.x >> 6; blk < nblk; blk += nwaves) {
         const int c = wg_c0 + 4 * blk + (lane >> 4);
         uint16_t *dst = As + blk * 64 * kChunk;
-        if (c < p.nfull)
-            lds_dma16(rowp + (int64_t)c * kChunk, dst);
-        else
+        if (c < p.nfull) {
+            if constexpr (RAW)
+                lds_dma16_raw<false>(rowp + (int64_t)c * kChunk, lds_addr_of(dst));
+            else
+                lds_dma16(rowp + (int64_t)c * kChunk, dst);
+        } else {
             sts16(dst + lane * kChunk, load_chunk_tail(rowp, c, p));
+        }
     }
 }
 
@@ -757,6 +789,183 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             [&](int b, int q, int rl) {
                 const int wq = rl / (16 * G);  // N-wave
                 const int t = (rl >> 4) % G;   // tile
+                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + (rl & 15) * 4;
+            },
+            [&](int m) { return 64 * (m >> 2) + (m & 3); });
+}
+
+// ---- MFMA kernel with an LDS ring --------------------------------------------
+// Same tiles, operands and epilogue as skg_mfma_kernel, but the loads write
+// straight into the wave's LDS tiles (global_load_lds_dwordx4) instead of a
+// register ring: a DMA instruction puts lane l's 16 bytes in slot l of a 1 KB
+// block (rows 4q .. 4q + 3 of the tile), so lane l fetches the chunk that
+// belongs in that slot of the XOR-swizzled tile, chunk (l & 15) ^ r of row
+// r = 4q + (l >> 4).  Each quarter-wave still reads one 256-byte row segment
+// (in permuted lane order), the tile needs no transposing writes, and the
+// ring costs LDS rather than VGPRs.  PF ring slots of G B tiles (plus one
+// activation tile when AQ > 0) per wave; K-tail masks are applied to the
+// operands as they are read.  Tokens m >= M read row M - 1 of A and produce
+// accumulator rows that are never stored (an MFMA output row depends on its
+// own activation row only).
+template <int G, int PF, int AQ>
+__global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p) {
+    constexpr bool AG = AQ > 0;
+    constexpr int NT = G + (AG ? 1 : 0);  // tiles per ring slot
+    constexpr int L = 4 * G + AQ;         // loads per K step
+    static_assert((PF - 1) * L < 64 && PF * L < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *As = reinterpret_cast<uint16_t *>(smem);
+    float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
+    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lo = lane & 15;
+    const int hi = lane >> 4;
+    const int wk = wave / p.waves_n;
+    const int wn = wave - wk * p.waves_n;
+    const WgPlan w = wg_plan(p);
+    const int NB = p.rows_per_wg;
+    const int M = p.M;
+    const int SPB = p.wave_chunks / kValuStep;
+    const int T = w.nblk * SPB;
+    const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
+    const int tail_st = max(0, (p.nfull - wv_c0) / kValuStep);
+    uint4 *ring = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (PF * NT * 256);
+    // chunk of the step fetched by this lane for DMA block q
+    int swz[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) swz[q] = lo ^ (4 * q + hi);
+    const uint16_t *arow[AG ? AQ : 1];
+#pragma unroll
+    for (int q = 0; q < (AG ? AQ : 1); ++q)
+        arow[q] = p.A + (int64_t)min(4 * q + hi, M - 1) * p.lda;
+
+    int lb = 0, lst = 0;
+    const uint16_t *rowp[G][4];
+    auto set_rows = [&](int b) {
+        const int rbase = (w.rb0 + b * w.rbs) * NB + wn * (16 * G) + hi;
+#pragma unroll
+        for (int t = 0; t < G; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                rowp[t][q] = (b < w.nblk)
+                                 ? p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb
+                                 : p.A;
+    };
+    const uint32_t ring_addr = lds_addr_of(ring);
+    auto issue = [&](int slot) {
+        const uint32_t dst = ring_addr + slot * (NT * kTileBytes);
+        const int cb0 = wv_c0 + lst * kValuStep;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t off = window_off(cb0 + swz[q], p);
+#pragma unroll
+            for (int t = 0; t < G; ++t)
+                lds_dma16_raw<true>(rowp[t][q] + off, dst + t * kTileBytes + 1024 * q);
+            if constexpr (AG)
+                if (q < AQ) lds_dma16_raw<false>(arow[q] + off, dst + G * kTileBytes + 1024 * q);
+        }
+        if (++lst == SPB) {
+            lst = 0;
+            set_rows(++lb);
+        }
+    };
+
+    set_rows(0);
+    if constexpr (!AG) stage_a_frag<true>(p, As, w.wg_c0);  // oldest loads
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue(i);
+    if constexpr (!AG) staged_barrier<PF * L>();
+
+    f32x4_t acc[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
+    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * 64 + lane;
+    const int st_block = p.waves_k * p.waves_n * G * 64;
+    const bool direct = direct_write(p);
+    const int rlw = wn * (16 * G);
+
+    int cb = 0, cst = 0;
+    auto step = [&](int slot) {
+        // this slot's loads are the oldest; the other PF - 1 steps stay in flight
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vmcnt<(PF - 1) * L>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const uint4 *tl = ring + slot * (NT * 256);
+        // all operands first, so the reads go out back to back
+        uint4 av[4], bv[4][G];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            av[s] = AG ? tl[G * 256 + tile_slot(lo, 4 * s + hi)]
+                       : lds16(ap + (cst * 4 + s) * (64 * kChunk));
+#pragma unroll
+            for (int t = 0; t < G; ++t) bv[s][t] = tl[t * 256 + tile_slot(lo, 4 * s + hi)];
+        }
+        if (cst >= tail_st) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + 4 * s + hi, p);
+                av[s] = and4(av[s], mk);
+#pragma unroll
+                for (int t = 0; t < G; ++t) bv[s][t] = and4(bv[s][t], mk);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < G; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, av[s]), __builtin_bit_cast(bf16x8_t, bv[s][t]),
+                    acc[t], 0, 0, 0);
+        if (++cst == SPB) {
+            const int rb = w.rb0 + cb * w.rbs;
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+                if (!direct) {
+                    st[cb * st_block + t * 64] = acc[t];
+                } else {
+                    int ln = lane;
+                    __asm__ volatile("" : "+v"(ln));
+                    const int rl = rlw + 16 * t + (ln & 15);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int m = 4 * (ln >> 4) + v;
+                        if (m < M) {
+                            if (p.split_k == 1) {
+                                if (rb * NB + rl < p.N) store_c(p, m, rb * NB + rl, acc[t][v]);
+                            } else {
+                                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
+                            }
+                        }
+                    }
+                }
+                acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            cst = 0;
+            ++cb;
+        }
+    };
+
+    // whole rounds: every slot is refilled right after it is read (refills
+    // past T read A and are never consumed)
+    const int TT = (T + PF - 1) / PF * PF;
+    for (int t0 = 0; t0 < TT; t0 += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            if (t0 + i < T) step(i);
+            issue(i);
+        }
+    }
+    // no LDS write may still be on its way when the workgroup's LDS is reused
+    wait_vmcnt<0>();
+    if (!direct)
+        write_blocks(
+            p, w, stash, flag,
+            [&](int b, int q, int rl) {
+                const int wq = rl / (16 * G);
+                const int t = (rl >> 4) % G;
                 return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + (rl & 15) * 4;
             },
             [&](int m) { return 64 * (m >> 2) + (m & 3); });

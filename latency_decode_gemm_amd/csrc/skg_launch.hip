@@ -96,9 +96,17 @@ struct MfmaVariant {
     KernelPtr lds_a;  // activations staged in LDS
     KernelPtr ga2;    // activations loaded from global memory, M <= 8
     KernelPtr ga4;    // activations loaded from global memory, M <= 16
+    KernelPtr ring_lds_a, ring_ga2, ring_ga4;  // the same with the LDS ring
 };
-#define SKG_MFMA(G, PF) \
-    {G, PF, skg_mfma_kernel<G, PF, 0>, skg_mfma_kernel<G, PF, 2>, skg_mfma_kernel<G, PF, 4>}
+#define SKG_MFMA(G, PF)                                                                 \
+    {G,                                                                                  \
+     PF,                                                                                 \
+     skg_mfma_kernel<G, PF, 0>,                                                          \
+     skg_mfma_kernel<G, PF, 2>,                                                          \
+     skg_mfma_kernel<G, PF, 4>,                                                          \
+     skg_mfma_ring_kernel<G, PF, 0>,                                                     \
+     skg_mfma_ring_kernel<G, PF, 2>,                                                     \
+     skg_mfma_ring_kernel<G, PF, 4>}
 const MfmaVariant kMfmaVariants[] = {SKG_MFMA(1, 2), SKG_MFMA(1, 3), SKG_MFMA(1, 4),
                                      SKG_MFMA(1, 6), SKG_MFMA(2, 1), SKG_MFMA(2, 2),
                                      SKG_MFMA(2, 3), SKG_MFMA(2, 4), SKG_MFMA(4, 1),
@@ -115,12 +123,16 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
             }
         return nullptr;
     }
-    if (inner == SKG_INNER_MFMA || inner == SKG_INNER_MFMA_GA) {
-        for (int i = 0; i < kNumMfma; ++i)
-            if (kMfmaVariants[i].G == row_tiles && kMfmaVariants[i].PF == depth)
-                return inner == SKG_INNER_MFMA ? kMfmaVariants[i].lds_a
-                       : M <= 8                ? kMfmaVariants[i].ga2
-                                               : kMfmaVariants[i].ga4;
+    for (int i = 0; i < kNumMfma; ++i) {
+        const MfmaVariant &v = kMfmaVariants[i];
+        if (v.G != row_tiles || v.PF != depth) continue;
+        switch (inner) {
+            case SKG_INNER_MFMA: return v.lds_a;
+            case SKG_INNER_MFMA_GA: return M <= 8 ? v.ga2 : v.ga4;
+            case SKG_INNER_MFMA_RING: return v.ring_lds_a;
+            case SKG_INNER_MFMA_RING_GA: return M <= 8 ? v.ring_ga2 : v.ring_ga4;
+            default: return nullptr;
+        }
     }
     return nullptr;
 }

@@ -40,7 +40,7 @@ def structures(skg, M, K, N, inner_set):
     """(inner, rt, depth, wn, wk, S, rb_per_wg) tuples for stage 1."""
     out = []
     mid_depth = {0: {1: 8, 2: 4, 4: 4}, 1: {1: 4, 2: 2, 4: 2}, 2: {1: 4, 2: 2, 4: 2},
-                 3: {1: 8, 2: 4, 4: 4}}
+                 3: {1: 8, 2: 4, 4: 4}, 4: {1: 4, 2: 2, 4: 2}, 5: {1: 4, 2: 2, 4: 2}}
     for inner in inner_set:
         for rt in (1, 2, 4):
             d = mid_depth[inner][rt]
@@ -216,8 +216,8 @@ def main():
             odt = skg.SKG_OUT_BF16 if out == "bf16" else skg.SKG_OUT_F32
             C = torch.zeros((M, ldc), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                             device="cuda")
-            inner_set = ([0, 3] if M < 2 else [0, 3, 1, 2] if M <= 8 else
-                         [0, 1, 2] if M <= 12 else [1, 2, 0])
+            inner_set = ([0, 3] if M < 2 else [0, 3, 1, 2, 4, 5] if M <= 8 else
+                         [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0])
             cands = structures(skg, M, K, N, inner_set)
             timed = {}
             for cfg in cands:

@@ -101,13 +101,37 @@ def test_check_config_rules():
     assert not skg.skinny_gemm_check_config(9, 7168, 256, mk(depth=4, **ga))
     assert not skg.skinny_gemm_check_config(8, 7168, 256, mk(depth=8, **ga))
     assert skg.skinny_gemm_check_config(2, 7168, 256, mk(depth=12, **ga))
+    assert not skg.skinny_gemm_check_config(4, 7168, 256, mk(inner=6, waves_k=4))  # no such inner
+
+
+def test_lds_ring_sizes():
+    """The LDS ring holds depth slots of 4 KB tiles per wave (row_tiles of B,
+    plus one of activations for the _GA kind), so it fits where the register
+    ring's single transpose tile per wave fits, minus what depth costs."""
+    mk = _capi.SkgConfig.make
+    # 8 waves x depth 4 x (1 + 1) tiles x 4 KB = 256 KB > 160 KB
+    deep = dict(split_k=1, row_tiles=1, waves_n=2, waves_k=4, depth=4)
+    assert skg.skinny_gemm_check_config(16, 7168, 256, mk(inner=skg.SKG_INNER_MFMA_GA, **deep))
+    assert not skg.skinny_gemm_check_config(16, 7168, 256,
+                                            mk(inner=skg.SKG_INNER_MFMA_RING_GA, **deep))
+    # 2 waves x depth 4 x 3 tiles x 4 KB = 96 KB
+    assert skg.skinny_gemm_check_config(16, 14336, 7168, mk(
+        inner=skg.SKG_INNER_MFMA_RING_GA, split_k=1, row_tiles=2, waves_n=1, waves_k=2, depth=4))
+    # staged A (1536 x 16 x 2 B = 48 KB) + 4 waves x depth 6 x 4 KB = 144 KB fits; depth 6
+    # with 6 waves (192 KB) does not
+    assert skg.skinny_gemm_check_config(16, 1536, 24576, mk(
+        inner=skg.SKG_INNER_MFMA_RING, split_k=1, row_tiles=1, waves_n=4, waves_k=1, depth=6))
+    assert not skg.skinny_gemm_check_config(16, 1536, 24576, mk(
+        inner=skg.SKG_INNER_MFMA_RING, split_k=1, row_tiles=1, waves_n=6, waves_k=1, depth=6))
 
 
 def test_compiled_variant_lists_match_library():
     for inner, allowed in ((skg.SKG_INNER_VALU, _capi.VALU_VARIANTS),
                            (skg.SKG_INNER_VALU_GA, [v for v in _capi.VALU_VARIANTS if 4 * v[1] <= 32]),
                            (skg.SKG_INNER_MFMA, _capi.MFMA_VARIANTS),
-                           (skg.SKG_INNER_MFMA_GA, _capi.MFMA_VARIANTS)):
+                           (skg.SKG_INNER_MFMA_GA, _capi.MFMA_VARIANTS),
+                           (skg.SKG_INNER_MFMA_RING, _capi.MFMA_VARIANTS),
+                           (skg.SKG_INNER_MFMA_RING_GA, _capi.MFMA_VARIANTS)):
         for rt in (1, 2, 3, 4, 8):
             for d in range(0, 10):
                 cfg = skg.SkgConfig.make(inner=inner, row_tiles=rt, depth=d, waves_k=2)

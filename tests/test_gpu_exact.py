@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 VG = skg.SKG_INNER_VALU_GA
+RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
 
 FAMILIES = [
     None,  # the dispatch table's choice
@@ -36,6 +37,11 @@ FAMILIES = [
     MK(inner=VG, split_k=1, row_tiles=2, waves_n=2, waves_k=4, depth=4),
     MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=VG, split_k=3, row_tiles=4, waves_n=1,
        waves_k=2, depth=2),
+    MK(inner=RF, split_k=1, row_tiles=1, waves_n=2, waves_k=2, depth=4),
+    MK(inner=RF, split_k=2, row_tiles=2, waves_n=1, waves_k=1, depth=2),
+    MK(inner=RG, split_k=1, row_tiles=2, waves_n=1, waves_k=2, depth=3),
+    MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=RG, split_k=3, row_tiles=1, waves_n=2,
+       waves_k=1, depth=6),
 ]
 
 
@@ -48,7 +54,7 @@ def _fid(c):
     if c is None:
         return "dispatch"
     return ("p2_" if c.backend == 2 else "") + \
-        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga"}[c.inner] + \
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
 
 

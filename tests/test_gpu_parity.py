@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 VG = skg.SKG_INNER_VALU_GA
+RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
 P2 = skg.SKG_BACKEND_SPLITK_2PASS
 
 
@@ -72,7 +73,12 @@ def _configs():
                 MK(inner=GA, split_k=3, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
                 MK(backend=P2, inner=GA, split_k=4, row_tiles=G, waves_n=1, waves_k=1, depth=PF,
                    rb_per_wg=2),
-                MK(backend=P2, inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=2, depth=PF)]
+                MK(backend=P2, inner=F, split_k=2, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
+                MK(inner=RF, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(inner=RF, split_k=2, row_tiles=G, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
+                MK(inner=RG, split_k=1, row_tiles=G, waves_n=2, waves_k=1, depth=PF, rb_per_wg=3),
+                MK(inner=RG, split_k=3, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
+                MK(backend=P2, inner=RG, split_k=2, row_tiles=G, waves_n=1, waves_k=1, depth=PF)]
     return out
 
 
@@ -82,7 +88,7 @@ SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 7
 
 def _cfg_id(c):
     return ("p2_" if c.backend == P2 else "") + \
-        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga"}[c.inner] + \
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_d{c.depth}_b{c.rb_per_wg}"
 
 
@@ -106,6 +112,37 @@ def test_forced_config(cfg):
             assert r["ok"], (M, K, N, out_dtype, r)
             ran += 1
     assert ran > 0
+
+
+@pytest.mark.parametrize("variant", list(skg._capi.MFMA_VARIANTS), ids=lambda v: f"G{v[0]}_d{v[1]}")
+def test_lds_ring_equals_register_ring(variant):
+    """The LDS-ring MFMA kernels issue the same MFMAs on the same operands in
+    the same order as the register-ring ones, so outputs agree bit for bit,
+    K tails, ragged N, every M and split-K included."""
+    torch = gu.torch_cuda()
+    G, PF = variant
+    ran = 0
+    for (M, K, N) in [(16, 1000, 333), (1, 2880, 200), (7, 136, 1000), (13, 8, 19), (16, 4104, 130)]:
+        ld = gu.round8(K)
+        A_bits = inputs.make_a(M, K, N, lda=ld)
+        B_bits = inputs.make_b(K, N, ldb=ld)
+        A, B = gu.operands(A_bits, B_bits, K)
+        for (reg, ring) in ((F, RF), (GA, RG)):
+            for (be, S, wn, wk, rpw) in ((0, 1, 1, 1, 1), (0, 1, 2, 2, 2), (1, 2, 1, 2, 1),
+                                         (P2, 3, 2, 1, 1)):
+                kw = dict(split_k=S, row_tiles=G, waves_n=wn, waves_k=wk, depth=PF, rb_per_wg=rpw)
+                c0 = MK(backend=be, inner=reg, **kw) if be else MK(inner=reg, **kw)
+                c1 = MK(backend=be, inner=ring, **kw) if be else MK(inner=ring, **kw)
+                if not (skg.skinny_gemm_check_config(M, K, N, c0)
+                        and skg.skinny_gemm_check_config(M, K, N, c1)):
+                    continue
+                want = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, c0))
+                out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+                skg.skinny_gemm_bf16_with_config(A, B, c1, out=out)
+                torch.cuda.synchronize()
+                assert np.array_equal(gu.bits_of(out), want), (M, K, N, c1)
+                ran += 1
+    assert ran >= 8
 
 
 @pytest.mark.parametrize("variant", list(skg._capi.VALU_VARIANTS),
