@@ -46,8 +46,10 @@ MALL_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30  # footprint between two uses of one weight copy
 DEFAULT_WORKLOAD = "wide_deep"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# what the counters depend on: the kernels' code (the configuration they were
+# taken with is stored beside them and compared separately)
 KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
-                  "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_api.cpp", "tuned_table.inc"]
+                  "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -310,7 +312,7 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
     return table
 
 
-def load_traffic(dominant_name):
+def load_traffic(dominant_name, config):
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -319,7 +321,7 @@ def load_traffic(dominant_name):
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     entry = t.get("points", {}).get(dominant_name)
-    if not entry:
+    if not entry or entry.get("config") != config:
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -416,7 +418,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    traffic = load_traffic(dom.name())
+    traffic = load_traffic(dom.name(), dom.cfg.as_dict())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic,

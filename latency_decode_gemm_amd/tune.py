@@ -39,11 +39,13 @@ def rows_per_wave(inner, rt):
 def structures(skg, M, K, N, inner_set):
     """(inner, rt, depth, wn, wk, S, rb_per_wg) tuples for stage 1."""
     out = []
-    mid_depth = {0: {1: 8, 2: 4, 4: 4}, 1: {1: 4, 2: 2, 4: 2}, 2: {1: 4, 2: 2, 4: 2},
-                 3: {1: 8, 2: 4, 4: 4}, 4: {1: 4, 2: 2, 4: 2}, 5: {1: 4, 2: 2, 4: 2}}
+    # two ring depths per structure (a shallow ring often wins when a
+    # workgroup streams few steps)
+    valu_d = {1: (4, 8), 2: (2, 4), 4: (2, 4)}
+    mfma_d = {1: (2, 4), 2: (1, 2), 4: (1, 2)}
     for inner in inner_set:
-        for rt in (1, 2, 4):
-            d = mid_depth[inner][rt]
+        depths = valu_d if inner in (0, 3) else mfma_d
+        for rt, d in [(rt, d) for rt in (1, 2, 4) for d in depths[rt]]:
             for (wn, wk) in WAVES:
                 nb = rows_per_wave(inner, rt) * wn
                 num_rb = math.ceil(N / nb)
@@ -236,8 +238,23 @@ def main():
             default = skg.skinny_gemm_dispatch(M, K, N)
             if default not in final:
                 final.append(default)
+            # and the best single dispatches, timed again with more repeats
+            for c in [c for c in sorted(timed, key=timed.get) if c.backend != 2][:3]:
+                if c not in final:
+                    final.append(c)
             refined = {cfg: time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg, stream,
                                         args.calls, reps=4) for cfg in final}
+            # A two-pass split (two dispatches) must beat the best single
+            # dispatch by 10%: its two kernel times, as a profiler sums them,
+            # run ~10-40% above what graph replay shows (the second kernel's
+            # start and ramp), while a single dispatch's do not.
+            raw = dict(refined)
+            singles = [c for c in refined if c.backend != 2]
+            if singles:
+                t1 = min(refined[c] for c in singles)
+                for c in refined:
+                    if c.backend == 2 and refined[c] > 0.90 * t1:
+                        refined[c] = float("inf")
             chosen = None
             for cfg in sorted(refined, key=refined.get):
                 C.fill_(float("nan"))
@@ -248,8 +265,8 @@ def main():
                     chosen = cfg
                     break
                 print(f"  parity failed for {cfg}: {r}", flush=True)
-            t_def = refined[default]
-            us = refined[chosen]
+            t_def = raw[default]
+            us = raw[chosen]
             wgbs = 2 * N * K / us / 1e3
             print(f"M={M:2d} K={K:5d} N={N:5d}: best {us:8.2f} us ({wgbs:7.1f} GB/s, "
                   f"{wgbs / 8000:.3f} of 8 TB/s)  current dispatch {t_def:8.2f} us  "
