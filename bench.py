@@ -199,6 +199,17 @@ def time_points_eager(torch, lib, pts, stream, calls=200, warm=20):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(oracle, pts, bpool, budget_s):
     """The oracle over the whole workload (every output), repeated until the
     time budget is used; rate = weight bytes per second."""
@@ -214,7 +225,8 @@ def cpu_baseline(oracle, pts, bpool, budget_s):
     return {"value": round(bytes_total / t_total / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole workload ({len(pts)} calls, every output), {passes} pass(es), "
-                      f"{t_total:.1f} s; binary64 C loop, OpenMP over columns"}
+                      f"{t_total:.1f} s; binary64 C loop, OpenMP over columns; "
+                      f"{threads} threads of {os.cpu_count()} logical CPUs, {cpu_model()}"}
 
 
 def oracle_mod():

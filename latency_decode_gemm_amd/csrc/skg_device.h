@@ -85,25 +85,30 @@ __device__ __forceinline__ void lds_dma16(const uint16_t *gsrc, void *lds_base) 
 // alias such a write (so a ring of them would never have more than one step
 // in flight).  The caller waits for the data itself (wait_vmcnt).  lds_addr
 // is the wave-uniform LDS byte address of lane 0's 16 bytes; NT marks the
-// load non-temporal (weights, read once).
+// load non-temporal (weights, read once).  m0 is set inside the statement
+// (one wait state before the load reads it); in the kernels that use this,
+// no compiler-generated instruction reads m0.
 __device__ __forceinline__ uint32_t lds_addr_of(const void *lds_ptr) {
     typedef __attribute__((address_space(3))) const void *lptr_t;
     return __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lptr_t)(lds_ptr));
 }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 in the clobber list
 template <bool NT>
 __device__ __forceinline__ void lds_dma16_raw(const uint16_t *gsrc, uint32_t lds_addr) {
     if constexpr (NT)
-        __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+        __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                          :
                          : "v"(gsrc), "s"(lds_addr)
                          : "memory", "m0");
     else
-        __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+        __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                          :
                          : "v"(gsrc), "s"(lds_addr)
                          : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Workgroup barrier that orders LDS accesses only: outstanding global loads
 // stay in flight across it.
