@@ -86,6 +86,28 @@ def variants_of(skg, M, K, N, cfg):
     return out
 
 
+TWO_PASS_MARGIN = 0.90
+
+
+def choose(timed, parity_ok):
+    """The fastest configuration of ``timed`` ({config: us per call}) that
+    passes ``parity_ok``.  A two-pass split (backend 2, two dispatches) counts
+    only if it beats the best single dispatch by 10%: graph replay hides its
+    second kernel's start, but its two kernel times, as a profiler sums them,
+    run 10-40% above a single dispatch's at equal graph time."""
+    t = dict(timed)
+    singles = [c for c in t if c.backend != 2]
+    if singles:
+        t1 = min(t[c] for c in singles)
+        for c in t:
+            if c.backend == 2 and t[c] > TWO_PASS_MARGIN * t1:
+                t[c] = float("inf")
+    for cfg in sorted(t, key=t.get):
+        if parity_ok(cfg):
+            return cfg
+    return None
+
+
 class Bench:
     """Rotating weight copies and a timing helper for one (K, N)."""
 
@@ -244,27 +266,20 @@ def main():
                     final.append(c)
             refined = {cfg: time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg, stream,
                                         args.calls, reps=4) for cfg in final}
-            # A two-pass split (two dispatches) must beat the best single
-            # dispatch by 10%: its two kernel times, as a profiler sums them,
-            # run ~10-40% above what graph replay shows (the second kernel's
-            # start and ramp), while a single dispatch's do not.
             raw = dict(refined)
-            singles = [c for c in refined if c.backend != 2]
-            if singles:
-                t1 = min(refined[c] for c in singles)
-                for c in refined:
-                    if c.backend == 2 and refined[c] > 0.90 * t1:
-                        refined[c] = float("inf")
-            chosen = None
-            for cfg in sorted(refined, key=refined.get):
+
+            def parity_ok(cfg):
                 C.fill_(float("nan"))
                 skg.skinny_gemm_bf16_with_config(A, bench.copies[0], cfg, out=C[:, :N])
                 torch.cuda.synchronize()
                 r = sampled_parity(oracle, acceptance, np, A_bits, bench.bits, C, M, K, N, out)
-                if r["ok"]:
-                    chosen = cfg
-                    break
-                print(f"  parity failed for {cfg}: {r}", flush=True)
+                if not r["ok"]:
+                    print(f"  parity failed for {cfg}: {r}", flush=True)
+                return r["ok"]
+
+            chosen = choose(refined, parity_ok)
+            if chosen is None:
+                raise RuntimeError(f"no configuration of M={M} K={K} N={N} matches the oracle")
             t_def = raw[default]
             us = raw[chosen]
             wgbs = 2 * N * K / us / 1e3
