@@ -150,3 +150,39 @@ def test_timed_entry_records_kernel_duration():
         outer.append(s0.elapsed_time(s1))
     assert min(durs) > 0.0
     assert np.median(durs) <= np.median(outer) * 1.02
+
+
+def test_graph_capture_lds_ring():
+    """LDS-ring MFMA calls (both kinds, one with a K tail) captured in a
+    graph: every replay equals the eager result."""
+    torch = gu.torch_cuda()
+    cases = [(16, 1536, 2048, MK(inner=skg.SKG_INNER_MFMA_RING_GA, split_k=1, row_tiles=1,
+                                 waves_n=3, waves_k=1, depth=3, rb_per_wg=2)),
+             (8, 1000, 333, MK(inner=skg.SKG_INNER_MFMA_RING, split_k=1, row_tiles=1,
+                               waves_n=2, waves_k=2, depth=4))]
+    s = torch.cuda.Stream()
+    probs, eager, outs = [], [], []
+    for (M, K, N, cfg) in cases:
+        ld = gu.round8(K)
+        A, B = gu.operands(inputs.make_a(M, K, N, lda=ld), inputs.make_b(K, N, ldb=ld), K)
+        with torch.cuda.stream(s):
+            eager.append(gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg, stream=s)))
+        probs.append((A, B, cfg))
+        outs.append(torch.empty((M, N), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for (A, B, cfg), out in zip(probs, outs):
+            skg.skinny_gemm_bf16_with_config(A, B, cfg, out=out, stream=s)
+    for i in range(4):
+        for out in outs:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for out, e in zip(outs, eager):
+            assert np.array_equal(gu.bits_of(out), e), i
+        with torch.cuda.stream(s):
+            A, B, cfg = probs[0]
+            skg.skinny_gemm_bf16_with_config(A, B, cfg, stream=s)
+        torch.cuda.synchronize()
