@@ -165,6 +165,28 @@ def test_maximum_m_and_large_n():
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("shape, cfg", [
+    ((16, 65536, 384), None),              # long K through the default rule
+    ((4, 64, 1 << 20), None),              # a million rows of B, tiny K
+    ((16, 1536, 98304), dict(inner=skg.SKG_INNER_MFMA_RING_GA, split_k=1, row_tiles=1,
+                             waves_n=3, waves_k=1, depth=3, rb_per_wg=2)),  # 302 MB of B
+], ids=["longK", "millionN", "ring302MB"])
+def test_large_shapes(shape, cfg):
+    torch = gu.torch_cuda()
+    M, K, N = shape
+    A_bits = inputs.make_a(M, K, N)
+    B_bits = inputs.make_b(K, N)
+    A, B = gu.operands(A_bits, B_bits, K)
+    if cfg is None:
+        C = skg.skinny_gemm_bf16(A, B, out_dtype=torch.bfloat16)
+    else:
+        C = skg.skinny_gemm_bf16_with_config(A, B, skg.SkgConfig.make(**cfg),
+                                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    r = gu.assess(C, A_bits, B_bits, K)
+    assert r["ok"], r
+
+
 def test_error_returns():
     torch = gu.torch_cuda()
     A17 = torch.zeros((17, 64), dtype=torch.bfloat16, device="cuda")
