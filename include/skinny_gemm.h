@@ -68,8 +68,16 @@ typedef enum {
     SKG_BACKEND_SPLITK = 1, /* split_k workgroups per row block, each one slice of K;
                                fp32 partials are summed in a fixed order by the
                                last workgroup to finish (no spin-wait) */
-    SKG_BACKEND_SPLITK_2PASS = 2 /* as SPLITK, but a second kernel on the same
-                                    stream sums the partials in split order */
+    SKG_BACKEND_SPLITK_2PASS = 2, /* as SPLITK, but a second kernel on the same
+                                     stream sums the partials in split order */
+    SKG_BACKEND_EVEN = 3 /* no K split; the N rows are dealt evenly to
+                            G = min(N, 256 * rb_per_wg) workgroups (256 CUs:
+                            rb_per_wg workgroups per CU), one row block of
+                            floor or ceil(N / G) rows each; rows_per_wg (the
+                            rows the waves cover) must be at least ceil(N / G).
+                            Lanes past a block's last row re-read that row
+                            (the same addresses within one load instruction,
+                            so no extra memory traffic) and store nothing */
 } skg_backend;
 
 typedef enum {

@@ -4,7 +4,7 @@ The computation runs in ``libskinny_gemm.so`` (hand-written HIP kernels behind
 the C ABI in ``include/skinny_gemm.h``); this package only marshals PyTorch
 tensors into that ABI.  ``inputs`` holds the seeded synthetic-input recipe.
 """
-from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_SPLITK, SKG_BACKEND_SPLITK_2PASS, SKG_ERR_HIP, SKG_ERR_INVALID_ARG,
+from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_EVEN, SKG_BACKEND_SPLITK, SKG_BACKEND_SPLITK_2PASS, SKG_ERR_HIP, SKG_ERR_INVALID_ARG,
                     SKG_ERR_MISALIGNED, SKG_ERR_NO_DEVICE, SKG_ERR_NOT_WARMED,
                     SKG_ERR_UNSUPPORTED, SKG_INNER_MFMA, SKG_INNER_MFMA_GA,
                     SKG_INNER_MFMA_RING, SKG_INNER_MFMA_RING_GA, SKG_INNER_VALU,

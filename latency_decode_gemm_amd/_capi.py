@@ -26,6 +26,7 @@ SKG_OUT_BF16 = 1
 SKG_BACKEND_DOT = 0
 SKG_BACKEND_SPLITK = 1
 SKG_BACKEND_SPLITK_2PASS = 2
+SKG_BACKEND_EVEN = 3
 SKG_INNER_VALU = 0
 SKG_INNER_MFMA = 1
 SKG_INNER_MFMA_GA = 2

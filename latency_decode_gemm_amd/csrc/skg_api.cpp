@@ -186,6 +186,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.nfull = g.nfull;
     p.split_k = cfg.split_k;
     p.two_pass = (cfg.backend == SKG_BACKEND_SPLITK_2PASS);
+    p.even = (cfg.backend == SKG_BACKEND_EVEN);
     p.wg_chunks = g.wg_chunks;
     p.wave_chunks = g.wave_chunks;
     p.waves_n = cfg.waves_n;
@@ -210,7 +211,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
 
 bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (M < 1 || M > SKG_MAX_M || K < 0 || N < 1) return false;
-    if (cfg.backend == SKG_BACKEND_DOT) {
+    if (cfg.backend == SKG_BACKEND_DOT || cfg.backend == SKG_BACKEND_EVEN) {
         if (cfg.split_k != 1) return false;
     } else if (cfg.backend == SKG_BACKEND_SPLITK || cfg.backend == SKG_BACKEND_SPLITK_2PASS) {
         if (cfg.split_k < 2 || cfg.split_k > 4096) return false;
@@ -232,8 +233,16 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.nfull = K / kChunk;
     r.rows_per_wave = valu ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
     r.rows_per_wg = r.rows_per_wave * cfg.waves_n;
-    r.num_rb = ceil_div(N, r.rows_per_wg);
-    r.grid_rb = ceil_div(r.num_rb, cfg.rb_per_wg);
+    if (cfg.backend == SKG_BACKEND_EVEN) {
+        // rows dealt evenly to 256 x rb_per_wg workgroups, one block each
+        if (cfg.rb_per_wg > 64) return false;
+        r.num_rb = std::min(N, kEvenUnit * cfg.rb_per_wg);
+        if (ceil_div(N, r.num_rb) > r.rows_per_wg) return false;
+        r.grid_rb = r.num_rb;
+    } else {
+        r.num_rb = ceil_div(N, r.rows_per_wg);
+        r.grid_rb = ceil_div(r.num_rb, cfg.rb_per_wg);
+    }
     const int S = cfg.split_k;
     const int per_split = ceil_div(std::max(r.nck, 1), S);
     r.wave_chunks = round_up(ceil_div(per_split, cfg.waves_k), r.step);

@@ -335,6 +335,20 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
     return w;
 }
 
+// Rows of row block rb: [start, start + count).  Uniform blocks of
+// rows_per_wg rows (the last one cut at N), or, with SKG_BACKEND_EVEN, the N
+// rows dealt evenly over num_rb blocks.  Loads clamp a local row to
+// count - 1; stores take local rows < count only.
+__device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start, int &count) {
+    if (p.even) {
+        start = (int)(((int64_t)rb * p.N) / p.num_rb);
+        count = (int)(((int64_t)(rb + 1) * p.N) / p.num_rb) - start;
+    } else {
+        start = rb * p.rows_per_wg;
+        count = min(p.rows_per_wg, p.N - start);
+    }
+}
+
 // ---- epilogue ------------------------------------------------------------------
 // A row block whose K range is covered by one wave is written straight from
 // that wave's registers.  Otherwise (waves_k > 1, or the single-pass split-K
@@ -362,14 +376,15 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
     const int mstep = blockDim.x / NB;
     for (int b = 0; b < w.nblk; ++b) {
         const int rb = w.rb0 + b * w.rbs;
-        const int row = rb * NB + rl;
+        int bst, bcnt;
+        block_rows(p, rb, bst, bcnt);
         float *part = (p.split_k > 1) ? p.ws + (size_t)(rb * p.split_k + w.s) * M * NB + rl
                                       : nullptr;
         for (int m = m0; m < M; m += mstep) {
             float v = stash[base(b, 0, rl) + mofs(m)];
             for (int q = 1; q < p.waves_k; ++q) v += stash[base(b, q, rl) + mofs(m)];
             if (p.split_k == 1) {
-                if (row < p.N) store_c(p, m, row, v);
+                if (rl < bcnt) store_c(p, m, bst + rl, v);
             } else if (p.two_pass) {
                 part[m * NB] = v;
             } else {
@@ -443,10 +458,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     int lb = 0, lst = 0;
     const uint16_t *rowp[R];
     auto set_rows = [&](int b) {
-        const int rbase = (w.rb0 + b * w.rbs) * NB + rl0;
+        int bst = 0, bcnt = 1;
+        if (b < w.nblk) block_rows(p, w.rb0 + b * w.rbs, bst, bcnt);
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            rowp[r] = (b < w.nblk) ? p.B + (int64_t)min(rbase + 4 * r, p.N - 1) * p.ldb : p.A;
+            rowp[r] = (b < w.nblk) ? p.B + (int64_t)(bst + min(rl0 + 4 * r, bcnt - 1)) * p.ldb
+                                   : p.A;
     };
     constexpr int NA = AG ? M : 1;
     auto issue = [&](uint4(&dst)[R], uint4(&adst)[NA]) {
@@ -516,6 +533,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         if (++cst == SPB) {
             // row block done: lane m of each row group now takes token m
             const int rb = w.rb0 + cb * w.rbs;
+            int bst, bcnt;
+            block_rows(p, rb, bst, bcnt);
             float *dst = stash + cb * per_block + (wk * M + l16) * NB + rl0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -527,8 +546,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
                     if (!direct) {
                         dst[4 * r] = v[0];
                     } else if (p.split_k == 1) {
-                        const int row = rb * NB + rl0 + 4 * r;
-                        if (row < p.N) store_c(p, l16, row, v[0]);
+                        if (rl0 + 4 * r < bcnt) store_c(p, l16, bst + rl0 + 4 * r, v[0]);
                     } else {
                         p.ws[((size_t)(rb * p.split_k + w.s) * M + l16) * NB + rl0 + 4 * r] = v[0];
                     }
@@ -649,13 +667,15 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     int lb = 0, lst = 0;
     const uint16_t *rowp[G][4];
     auto set_rows = [&](int b) {
-        const int rbase = (w.rb0 + b * w.rbs) * NB + wn * (16 * G) + hi;
+        int bst = 0, bcnt = 1;
+        if (b < w.nblk) block_rows(p, w.rb0 + b * w.rbs, bst, bcnt);
+        const int rl = wn * (16 * G) + hi;
 #pragma unroll
         for (int t = 0; t < G; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 rowp[t][q] = (b < w.nblk)
-                                 ? p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb
+                                 ? p.B + (int64_t)(bst + min(rl + 16 * t + 4 * q, bcnt - 1)) * p.ldb
                                  : p.A;
     };
     auto issue = [&](uint4(&dst)[G][4], uint4(&adst)[NA]) {
@@ -748,6 +768,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
         if (++cst == SPB) {
             // acc[t][v] holds token 4*hi + v of local row rlw + 16*t + lo
             const int rb = w.rb0 + cb * w.rbs;
+            int bst, bcnt;
+            block_rows(p, rb, bst, bcnt);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
                 if (!direct) {
@@ -763,7 +785,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                         const int m = 4 * (ln >> 4) + v;
                         if (m < M) {
                             if (p.split_k == 1) {
-                                if (rb * NB + rl < p.N) store_c(p, m, rb * NB + rl, acc[t][v]);
+                                if (rl < bcnt) store_c(p, m, bst + rl, acc[t][v]);
                             } else {
                                 p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
                             }
@@ -849,13 +871,15 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     int lb = 0, lst = 0;
     const uint16_t *rowp[G][4];
     auto set_rows = [&](int b) {
-        const int rbase = (w.rb0 + b * w.rbs) * NB + wn * (16 * G) + hi;
+        int bst = 0, bcnt = 1;
+        if (b < w.nblk) block_rows(p, w.rb0 + b * w.rbs, bst, bcnt);
+        const int rl = wn * (16 * G) + hi;
 #pragma unroll
         for (int t = 0; t < G; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 rowp[t][q] = (b < w.nblk)
-                                 ? p.B + (int64_t)min(rbase + 16 * t + 4 * q, p.N - 1) * p.ldb
+                                 ? p.B + (int64_t)(bst + min(rl + 16 * t + 4 * q, bcnt - 1)) * p.ldb
                                  : p.A;
     };
     const uint32_t ring_addr = lds_addr_of(ring);
@@ -926,6 +950,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
                     acc[t], 0, 0, 0);
         if (++cst == SPB) {
             const int rb = w.rb0 + cb * w.rbs;
+            int bst, bcnt;
+            block_rows(p, rb, bst, bcnt);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
                 if (!direct) {
@@ -939,7 +965,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
                         const int m = 4 * (ln >> 4) + v;
                         if (m < M) {
                             if (p.split_k == 1) {
-                                if (rb * NB + rl < p.N) store_c(p, m, rb * NB + rl, acc[t][v]);
+                                if (rl < bcnt) store_c(p, m, bst + rl, acc[t][v]);
                             } else {
                                 p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
                             }

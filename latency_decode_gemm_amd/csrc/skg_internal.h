@@ -19,6 +19,8 @@ constexpr int kValuStep = 16;
 // gfx950 LDS per workgroup.
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
+// SKG_BACKEND_EVEN: workgroups per rb_per_wg (the CU count of MI355X)
+constexpr int kEvenUnit = 256;
 
 // Everything a kernel needs, passed by value.
 struct KParams {
@@ -34,6 +36,7 @@ struct KParams {
     int nfull;        // K / 8 (chunks with all 8 elements inside K)
     int split_k;      // workgroups along K per row block
     int two_pass;     // split-K partials are summed by a second kernel
+    int even;         // SKG_BACKEND_EVEN: row block rb is rows [rb N / num_rb, (rb + 1) N / num_rb)
     int wg_chunks;    // chunks per split (multiple of wave_chunks)
     int wave_chunks;  // chunks per K-wave (multiple of the K-step)
     int waves_n, waves_k;

@@ -67,6 +67,16 @@ def structures(skg, M, K, N, inner_set):
                                                      depth=d, rb_per_wg=rpw)
                             if skg.skinny_gemm_check_config(M, K, N, cfg):
                                 out.append(cfg)
+                # rows dealt evenly to 256 or 512 workgroups (backend 3), when
+                # the waves cover a block with little to spare
+                for per_cu in (1, 2):
+                    need = math.ceil(N / min(N, 256 * per_cu))
+                    if not need <= nb < 2 * need + 16:
+                        continue
+                    cfg = skg.SkgConfig.make(backend=3, inner=inner, split_k=1, row_tiles=rt,
+                                             waves_n=wn, waves_k=wk, depth=d, rb_per_wg=per_cu)
+                    if skg.skinny_gemm_check_config(M, K, N, cfg):
+                        out.append(cfg)
     return out
 
 

@@ -63,7 +63,8 @@ def test_dispatch_valid_on_a_shape_grid():
             for N in (1, 3, 16, 128, 129, 2112, 24576):
                 cfg = skg.skinny_gemm_dispatch(M, K, N)
                 assert skg.skinny_gemm_check_config(M, K, N, cfg), (M, K, N, cfg)
-                assert (cfg.backend == skg.SKG_BACKEND_DOT) == (cfg.split_k == 1)
+                assert (cfg.backend in (skg.SKG_BACKEND_DOT, skg.SKG_BACKEND_EVEN)) == \
+                    (cfg.split_k == 1)
 
 
 def test_dispatch_rejects():
@@ -102,6 +103,38 @@ def test_check_config_rules():
     assert not skg.skinny_gemm_check_config(8, 7168, 256, mk(depth=8, **ga))
     assert skg.skinny_gemm_check_config(2, 7168, 256, mk(depth=12, **ga))
     assert not skg.skinny_gemm_check_config(4, 7168, 256, mk(inner=6, waves_k=4))  # no such inner
+
+
+def test_even_backend_rules():
+    """SKG_BACKEND_EVEN: no K split; min(N, 256 x rb_per_wg) workgroups of
+    floor/ceil(N / G) rows, which the waves must cover; no workspace."""
+    mk = _capi.SkgConfig.make
+    ev = dict(backend=skg.SKG_BACKEND_EVEN, split_k=1, waves_k=2, depth=4)
+    # 2112 rows over 256 workgroups: up to 9 rows, 12 covered by 3 VALU waves
+    c = mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=3, rb_per_wg=1, **ev)
+    assert skg.skinny_gemm_check_config(2, 7168, 2112, c)
+    assert skg.skinny_gemm_workspace_bytes(2, 7168, 2112, c) == 0
+    # 8 rows cannot hold 9
+    assert not skg.skinny_gemm_check_config(
+        2, 7168, 2112, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=2, rb_per_wg=1, **ev))
+    # 512 workgroups: 5 rows each, 8 covered
+    assert skg.skinny_gemm_check_config(
+        2, 7168, 2112, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=2, rb_per_wg=2, **ev))
+    # 7168 rows over 256: 28 each, a 32-row MFMA wave covers them, a 16-row one does not
+    mf = dict(backend=skg.SKG_BACKEND_EVEN, split_k=1, waves_n=1, waves_k=2, rb_per_wg=1)
+    assert skg.skinny_gemm_check_config(16, 14336, 7168, mk(inner=skg.SKG_INNER_MFMA_GA,
+                                                            row_tiles=2, depth=3, **mf))
+    assert not skg.skinny_gemm_check_config(16, 14336, 7168, mk(inner=skg.SKG_INNER_MFMA_GA,
+                                                                row_tiles=1, depth=4, **mf))
+    # fewer rows than workgroups: one row each
+    assert skg.skinny_gemm_check_config(
+        1, 64, 100, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=1, rb_per_wg=1, **ev))
+    # no K split, and at most 64 workgroups per CU
+    assert not skg.skinny_gemm_check_config(
+        2, 7168, 2112, mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_VALU, split_k=2,
+                          row_tiles=1, waves_n=3, waves_k=2, depth=4))
+    assert not skg.skinny_gemm_check_config(
+        2, 7168, 2112, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=3, rb_per_wg=65, **ev))
 
 
 def test_lds_ring_sizes():

@@ -38,6 +38,10 @@ FAMILIES = [
     MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=VG, split_k=3, row_tiles=4, waves_n=1,
        waves_k=2, depth=2),
     MK(inner=RF, split_k=1, row_tiles=1, waves_n=2, waves_k=2, depth=4),
+    MK(backend=skg.SKG_BACKEND_EVEN, inner=V, split_k=1, row_tiles=2, waves_n=2, waves_k=2,
+       depth=4),
+    MK(backend=skg.SKG_BACKEND_EVEN, inner=GA, split_k=1, row_tiles=1, waves_n=2, waves_k=1,
+       depth=3),
     MK(inner=RF, split_k=2, row_tiles=2, waves_n=1, waves_k=1, depth=2),
     MK(inner=RG, split_k=1, row_tiles=2, waves_n=1, waves_k=2, depth=3),
     MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=RG, split_k=3, row_tiles=1, waves_n=2,
@@ -53,7 +57,7 @@ def _m_for(cfg, m):
 def _fid(c):
     if c is None:
         return "dispatch"
-    return ("p2_" if c.backend == 2 else "") + \
+    return ("p2_" if c.backend == 2 else "ev_" if c.backend == 3 else "") + \
         {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
 

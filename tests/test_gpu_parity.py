@@ -20,6 +20,7 @@ V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 VG = skg.SKG_INNER_VALU_GA
 RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
 P2 = skg.SKG_BACKEND_SPLITK_2PASS
+EV = skg.SKG_BACKEND_EVEN
 
 
 def _run_point(p):
@@ -62,7 +63,9 @@ def _configs():
                 MK(inner=VG, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
                 MK(inner=VG, split_k=1, row_tiles=R, waves_n=2, waves_k=3, depth=PF, rb_per_wg=3),
                 MK(inner=VG, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
-                MK(backend=P2, inner=VG, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF)]
+                MK(backend=P2, inner=VG, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF),
+                MK(backend=EV, inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=2, depth=PF),
+                MK(backend=EV, inner=VG, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF)]
     for (G, PF) in skg._capi.MFMA_VARIANTS:
         out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 # 8 waves of 4 transpose tiles each would not leave LDS for A
@@ -78,7 +81,10 @@ def _configs():
                 MK(inner=RF, split_k=2, row_tiles=G, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
                 MK(inner=RG, split_k=1, row_tiles=G, waves_n=2, waves_k=1, depth=PF, rb_per_wg=3),
                 MK(inner=RG, split_k=3, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
-                MK(backend=P2, inner=RG, split_k=2, row_tiles=G, waves_n=1, waves_k=1, depth=PF)]
+                MK(backend=P2, inner=RG, split_k=2, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(backend=EV, inner=GA, split_k=1, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
+                MK(backend=EV, inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=1, depth=PF),
+                MK(backend=EV, inner=RG, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF)]
     return out
 
 
@@ -87,7 +93,7 @@ SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 7
 
 
 def _cfg_id(c):
-    return ("p2_" if c.backend == P2 else "") + \
+    return ("p2_" if c.backend == P2 else "ev_" if c.backend == EV else "") + \
         {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_d{c.depth}_b{c.rb_per_wg}"
 
