@@ -9,24 +9,27 @@
 // not translated from that design:
 //
 //  * One launch streams B exactly once.  Rows of B are grouped in row blocks
-//    of rows_per_wg rows; K is cut into split_k slices.  A workgroup owns one
-//    K slice and a strided set of row blocks (blockIdx / split_k, then every
-//    gridDim / split_k-th), so it stages A[:, slice] in LDS once (zero beyond
-//    K) and then streams all of its row blocks.  Its waves split the rows of a
-//    block (waves_n) and the slice (waves_k, equal parts).
+//    of rows_per_wg rows (or dealt evenly, one block per workgroup); K is cut
+//    into split_k slices.  A workgroup owns one K slice and a strided set of
+//    row blocks (blockIdx / split_k, then every gridDim / split_k-th), so it
+//    stages A[:, slice] in LDS once (zero beyond K) and then streams all of
+//    its row blocks.  Its waves split the rows of a block (waves_n) and the
+//    slice (waves_k, equal parts).
 //  * Every wave runs one flat stream of K steps over all its row blocks, with
-//    `depth` steps of B loads in flight in a register ring; the loads of the
-//    next row block are already in flight while the current block is reduced
-//    and written.  Barriers inside that stream wait for LDS traffic only, so
-//    they never drain the ring.
+//    `depth` steps of B loads in flight in a register ring (or, in the
+//    LDS-ring MFMA kernel, in LDS tiles filled by direct global-to-LDS
+//    loads); the loads of the next row block are already in flight while the
+//    current block is reduced and written.  Barriers inside that stream wait
+//    for LDS traffic only, so they never drain the ring.
 //  * VALU inner product: 16 lanes per row of B, so one 64-lane dwordx4 load
 //    covers 4 rows x 256 contiguous bytes; products by v_dot2c_f32_bf16 (two
 //    bf16 products added into fp32).  The 16 lanes of a row are combined with
 //    a DPP reduce-scatter (row_mirror, row_half_mirror, quad_perm) that leaves
 //    lane i of the row group with the sum for token m = i.
 //  * MFMA inner product (v_mfma_f32_16x16x32_bf16): the activations are the
-//    16-row operand (rows m >= M are zero), 16 rows of B are the 16 columns;
-//    the instruction performs the K reduction, so no cross-lane step remains.
+//    16-row operand (rows m >= M are never stored), 16 rows of B are the 16
+//    columns; the instruction performs the K reduction, so no cross-lane step
+//    remains.
 //  * Cross-wave (waves_k > 1): partials go through LDS (double-buffered per
 //    row block) and wave 0 adds them in wave order.  Cross-workgroup
 //    (split_k > 1): each workgroup stores its fp32 partial tile with
