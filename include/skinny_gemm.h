@@ -70,14 +70,18 @@ typedef enum {
                                last workgroup to finish (no spin-wait) */
     SKG_BACKEND_SPLITK_2PASS = 2, /* as SPLITK, but a second kernel on the same
                                      stream sums the partials in split order */
-    SKG_BACKEND_EVEN = 3 /* no K split; the N rows are dealt evenly to
-                            G = min(N, 256 * rb_per_wg) workgroups (256 CUs:
-                            rb_per_wg workgroups per CU), one row block of
-                            floor or ceil(N / G) rows each; rows_per_wg (the
-                            rows the waves cover) must be at least ceil(N / G).
-                            Lanes past a block's last row re-read that row
-                            (the same addresses within one load instruction,
-                            so no extra memory traffic) and store nothing */
+    SKG_BACKEND_EVEN = 3 /* 256 * rb_per_wg workgroups (256 CUs: rb_per_wg
+                            workgroups per CU) are G = min(N, 256 * rb_per_wg
+                            / split_k) row blocks times split_k K slices
+                            (split_k >= 1 must divide 256 * rb_per_wg); the N
+                            rows are dealt evenly to the G blocks, floor or
+                            ceil(N / G) rows each; rows_per_wg (the rows the
+                            waves cover) must be at least ceil(N / G).  Lanes
+                            past a block's last row re-read that row (the same
+                            addresses within one load instruction, so no extra
+                            memory traffic) and store nothing.  With split_k
+                            >= 2 the slices' fp32 partials are summed as in
+                            SKG_BACKEND_SPLITK */
 } skg_backend;
 
 typedef enum {
@@ -106,7 +110,8 @@ typedef enum {
  * skinny_gemm_bf16_with_config accepts.  Plain data; compare field by field. */
 typedef struct skg_config {
     int32_t backend;   /* skg_backend; SKG_BACKEND_DOT requires split_k == 1,
-                          the split-K backends require split_k >= 2 */
+                          the split-K backends require split_k >= 2,
+                          SKG_BACKEND_EVEN takes either */
     int32_t inner;     /* skg_inner */
     int32_t split_k;   /* workgroups along K per row block */
     int32_t row_tiles; /* rows per wave: VALU 4*row_tiles (1, 2, 4);
@@ -163,8 +168,9 @@ int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
 /* Whether cfg can run (M, K, N): SKG_OK or SKG_ERR_INVALID_ARG.  Pure host. */
 int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg);
 
-/* Bytes of split-K workspace (partials, plus tickets for SKG_BACKEND_SPLITK)
- * cfg needs for (M, K, N); 0 for SKG_BACKEND_DOT.  Pure host. */
+/* Bytes of split-K workspace (partials, plus tickets for the single-pass
+ * sum of SKG_BACKEND_SPLITK and of SKG_BACKEND_EVEN with split_k >= 2) cfg
+ * needs for (M, K, N); 0 without a K split.  Pure host. */
 int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg,
                                 size_t *bytes);
 

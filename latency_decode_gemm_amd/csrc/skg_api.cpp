@@ -211,8 +211,12 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
 
 bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (M < 1 || M > SKG_MAX_M || K < 0 || N < 1) return false;
-    if (cfg.backend == SKG_BACKEND_DOT || cfg.backend == SKG_BACKEND_EVEN) {
+    if (cfg.backend == SKG_BACKEND_DOT) {
         if (cfg.split_k != 1) return false;
+    } else if (cfg.backend == SKG_BACKEND_EVEN) {
+        // the 256 x rb_per_wg workgroups are num_rb row blocks x split_k slices
+        if (cfg.split_k < 1 || cfg.split_k > 64) return false;
+        if (cfg.rb_per_wg < 1 || (kEvenUnit * cfg.rb_per_wg) % cfg.split_k != 0) return false;
     } else if (cfg.backend == SKG_BACKEND_SPLITK || cfg.backend == SKG_BACKEND_SPLITK_2PASS) {
         if (cfg.split_k < 2 || cfg.split_k > 4096) return false;
     } else {
@@ -234,9 +238,10 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     r.rows_per_wave = valu ? 4 * cfg.row_tiles : 16 * cfg.row_tiles;
     r.rows_per_wg = r.rows_per_wave * cfg.waves_n;
     if (cfg.backend == SKG_BACKEND_EVEN) {
-        // rows dealt evenly to 256 x rb_per_wg workgroups, one block each
+        // rows dealt evenly to 256 x rb_per_wg / split_k row blocks, one
+        // workgroup per (row block, K slice)
         if (cfg.rb_per_wg > 64) return false;
-        r.num_rb = std::min(N, kEvenUnit * cfg.rb_per_wg);
+        r.num_rb = std::min(N, kEvenUnit * cfg.rb_per_wg / cfg.split_k);
         if (ceil_div(N, r.num_rb) > r.rows_per_wg) return false;
         r.grid_rb = r.num_rb;
     } else {
@@ -269,7 +274,9 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     const size_t per_block = valu ? (size_t)M * r.rows_per_wg : (size_t)16 * r.rows_per_wg;
     const size_t blocks_per_wg = (size_t)ceil_div(r.num_rb, r.grid_rb);
     // (a row block covered by one wave is written from registers)
-    const bool direct = cfg.waves_k == 1 && cfg.backend != SKG_BACKEND_SPLITK;
+    // (the single-pass split-K settles row blocks workgroup by workgroup)
+    const bool one_pass = cfg.split_k > 1 && cfg.backend != SKG_BACKEND_SPLITK_2PASS;
+    const bool direct = cfg.waves_k == 1 && !one_pass;
     const size_t stash_bytes =
         direct ? 0 : blocks_per_wg * cfg.waves_k * per_block * sizeof(float);
     if (r.stash_offset + stash_bytes > (size_t)kMaxLdsBytes) return false;
@@ -278,7 +285,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
     r.threads = 64 * cfg.waves_n * cfg.waves_k;
     r.ws_floats = (S > 1) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
-    r.n_tickets = (S > 1 && cfg.backend == SKG_BACKEND_SPLITK) ? (size_t)r.num_rb : 0;
+    r.n_tickets = one_pass ? (size_t)r.num_rb : 0;
     if ((int64_t)r.grid_rb * S > 0x7FFFFFFF) return false;
     *g = r;
     return true;

@@ -287,6 +287,20 @@ __device__ __forceinline__ float ws_load(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Rows of row block rb: [start, start + count).  Uniform blocks of
+// rows_per_wg rows (the last one cut at N), or, with SKG_BACKEND_EVEN, the N
+// rows dealt evenly over num_rb blocks.  Loads clamp a local row to
+// count - 1; stores take local rows < count only.
+__device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start, int &count) {
+    if (p.even) {
+        start = (int)(((int64_t)rb * p.N) / p.num_rb);
+        count = (int)(((int64_t)(rb + 1) * p.N) / p.num_rb) - start;
+    } else {
+        start = rb * p.rows_per_wg;
+        count = min(p.rows_per_wg, p.N - start);
+    }
+}
+
 // Called by every thread of the workgroup once this workgroup's partials of
 // row block rb are stored (ws_store) and complete (s_waitcnt) in the waves that
 // stored them.  The workgroup that draws the last ticket adds the split_k
@@ -303,14 +317,15 @@ __device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsign
         const int NB = p.rows_per_wg;
         const int total = p.M * NB;
         const float *base = p.ws + (size_t)rb * p.split_k * total;
+        int bst, bcnt;
+        block_rows(p, rb, bst, bcnt);
         for (int i = threadIdx.x; i < total; i += blockDim.x) {
             const int m = i / NB;
             const int rl = i - m * NB;
-            const int row = rb * NB + rl;
-            if (row < p.N) {
+            if (rl < bcnt) {
                 float v = 0.0f;
                 for (int s = 0; s < p.split_k; ++s) v += ws_load(base + (size_t)s * total + i);
-                store_c(p, m, row, v);
+                store_c(p, m, bst + rl, v);
             }
         }
         if (threadIdx.x == 0)
@@ -336,20 +351,6 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
     w.nblk = w.rb0 < p.num_rb ? (p.num_rb - w.rb0 + w.rbs - 1) / w.rbs : 0;
     w.wg_c0 = w.s * p.wg_chunks;
     return w;
-}
-
-// Rows of row block rb: [start, start + count).  Uniform blocks of
-// rows_per_wg rows (the last one cut at N), or, with SKG_BACKEND_EVEN, the N
-// rows dealt evenly over num_rb blocks.  Loads clamp a local row to
-// count - 1; stores take local rows < count only.
-__device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start, int &count) {
-    if (p.even) {
-        start = (int)(((int64_t)rb * p.N) / p.num_rb);
-        count = (int)(((int64_t)(rb + 1) * p.N) / p.num_rb) - start;
-    } else {
-        start = rb * p.rows_per_wg;
-        count = min(p.rows_per_wg, p.N - start);
-    }
 }
 
 // ---- epilogue ------------------------------------------------------------------

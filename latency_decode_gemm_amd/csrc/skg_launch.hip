@@ -69,7 +69,8 @@ __global__ void __launch_bounds__(256) skg_stream_read_kernel(const uint16_t *sr
 }
 
 // Second pass of SKG_BACKEND_SPLITK_2PASS: C[m][row] = sum over s (in split
-// order) of ws[((rb*S + s)*M + m)*NB + rl]; consecutive threads take
+// order) of ws[((rb*S + s)*M + m)*NB + rl], row = first row of block rb + rl
+// (only rl < the block's row count); consecutive threads take
 // consecutive rows, so partial reads and C writes are coalesced.
 __global__ void skg_splitk_reduce_kernel(KParams p) {
     const int NB = p.rows_per_wg;
@@ -81,12 +82,13 @@ __global__ void skg_splitk_reduce_kernel(KParams p) {
         const int rem = (int)(i - (int64_t)rb * per_rb);
         const int m = rem / NB;
         const int rl = rem - m * NB;
-        const int row = rb * NB + rl;
-        if (row < p.N) {
+        int bst, bcnt;
+        block_rows(p, rb, bst, bcnt);
+        if (rl < bcnt) {
             const float *src = p.ws + (size_t)rb * p.split_k * per_rb + rem;
             float v = 0.0f;
             for (int s = 0; s < p.split_k; ++s) v += src[(size_t)s * per_rb];
-            store_c(p, m, row, v);
+            store_c(p, m, bst + rl, v);
         }
     }
 }

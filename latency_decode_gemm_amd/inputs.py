@@ -76,6 +76,29 @@ def make_b(K: int, N: int, ldb: int | None = None, r: int = 0, seed: int | None 
     return _normal_bits(N, K, ldb, seed_b(K, N, r) if seed is None else seed, float(scale))
 
 
+PAD_F32 = np.uint32(0x7FC00001)  # quiet NaN, distinctive payload
+
+
+def make_w_f32(K: int, N: int, ldw: int | None = None, r: int = 0,
+               seed: int | None = None) -> np.ndarray:
+    """fp32 weights W[N, ldw] for the fp32-weight router GEMM: the same draws
+    z / sqrt(K) as make_b (same seed), kept in float32 instead of being
+    rounded to bf16; padding columns hold a quiet NaN."""
+    ldw = K if ldw is None else ldw
+    out = np.full((N, ldw), PAD_F32, dtype=np.uint32).view(np.float32)
+    if N == 0 or K == 0:
+        return out
+    gen = np.random.Generator(np.random.PCG64(seed_b(K, N, r) if seed is None else seed))
+    scale = np.float32(1.0 / np.sqrt(K))
+    step = max(1, (1 << 24) // K)
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        z = gen.standard_normal((r1 - r0, K), dtype=np.float32)
+        z *= scale
+        out[r0:r1, :K] = z
+    return out
+
+
 def make_inputs(M: int, K: int, N: int, lda: int | None = None, ldb: int | None = None,
                 r: int = 0):
     """(A_bits [M, lda], B_bits [N, ldb]) for one workload point."""
@@ -92,6 +115,14 @@ WORKLOADS = {
     "qkv_a_strided": [dict(M=m, K=7168, N=2112, out="bf16", ldc=4096) for m in (2, 3, 8, 16)],
     "wide_deep": [dict(M=m, K=k, N=n, out="bf16", ldc=None)
                   for (k, n) in ((1536, 24576), (14336, 7168)) for m in (1, 2, 4, 8, 16)],
+}
+
+
+# The router GEMM over fp32 weights (bf16 activations, fp32 output): the
+# router sweep's shapes.
+WORKLOADS_F32W = {
+    "router_f32w": [dict(M=m, K=7168, N=n, out="f32", ldc=None, w="f32")
+                    for n in (256, 384) for m in (1, 2, 3, 4, 8, 16)],
 }
 
 

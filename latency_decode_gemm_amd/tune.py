@@ -67,16 +67,19 @@ def structures(skg, M, K, N, inner_set):
                                                      depth=d, rb_per_wg=rpw)
                             if skg.skinny_gemm_check_config(M, K, N, cfg):
                                 out.append(cfg)
-                # rows dealt evenly to 256 or 512 workgroups (backend 3), when
-                # the waves cover a block with little to spare
+                # rows dealt evenly to 256 or 512 workgroups (backend 3), as
+                # row blocks x K slices, when the waves cover a block with
+                # little to spare
                 for per_cu in (1, 2):
-                    need = math.ceil(N / min(N, 256 * per_cu))
-                    if not need <= nb < 2 * need + 16:
-                        continue
-                    cfg = skg.SkgConfig.make(backend=3, inner=inner, split_k=1, row_tiles=rt,
-                                             waves_n=wn, waves_k=wk, depth=d, rb_per_wg=per_cu)
-                    if skg.skinny_gemm_check_config(M, K, N, cfg):
-                        out.append(cfg)
+                    for S in (1, 2, 4, 8):
+                        need = math.ceil(N / min(N, 256 * per_cu // S))
+                        if not need <= nb < 2 * need + 16:
+                            continue
+                        cfg = skg.SkgConfig.make(backend=3, inner=inner, split_k=S,
+                                                 row_tiles=rt, waves_n=wn, waves_k=wk, depth=d,
+                                                 rb_per_wg=per_cu)
+                        if skg.skinny_gemm_check_config(M, K, N, cfg):
+                            out.append(cfg)
     return out
 
 
@@ -180,6 +183,24 @@ def sampled_parity(oracle, acceptance, np, A_bits, B_bits, C, M, K, N, out):
     return acceptance.assess(Cf[:, ns], ref, an, bn, out)
 
 
+def read_table(path=TABLE):
+    """The entries of the compiled-in table as result records (so that a
+    partial retune keeps every point it did not time)."""
+    import re
+    pat = re.compile(r"\{(\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*// ([\d.]+) us")
+    keys = ("backend", "inner", "split_k", "row_tiles", "waves_n", "waves_k", "depth",
+            "rb_per_wg")
+    out = []
+    with open(path) as f:
+        for line in f:
+            m = pat.search(line)
+            if m:
+                vals = [int(v) for v in m.group(4).split(",")]
+                out.append({"M": int(m.group(1)), "K": int(m.group(2)), "N": int(m.group(3)),
+                            "us": float(m.group(5)), "config": dict(zip(keys, vals))})
+    return out
+
+
 def write_table(results, path=TABLE):
     lines = [
         "// Tuned (M, K, N) -> configuration table, measured on MI355X (gfx950) by",
@@ -231,7 +252,8 @@ def main():
         pts = [p for p in inputs.all_points() if (p["M"], p["K"], p["N"]) in want]
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
-    results = []
+    # points not timed in this run keep their current entries
+    results = read_table()
     if args.merge and os.path.exists(args.merge):
         with open(args.merge) as f:
             results = [r for r in json.load(f)["results"]]
@@ -254,9 +276,14 @@ def main():
                          [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0])
             cands = structures(skg, M, K, N, inner_set)
             timed = {}
-            for cfg in cands:
+            print(f"M={M} K={K} N={N}: {len(cands)} stage-1 candidates", file=sys.stderr,
+                  flush=True)
+            for i, cfg in enumerate(cands):
                 timed[cfg] = time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg, stream,
                                          args.calls, reps=1)
+                if i % 500 == 499:
+                    print(f"  {i + 1} timed, best {min(timed.values()):.2f} us", file=sys.stderr,
+                          flush=True)
             best = sorted(timed, key=timed.get)[:args.top]
             stage2 = set()
             for b in best:

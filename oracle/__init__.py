@@ -13,7 +13,13 @@ What it computes is the plain definition of the operation the pages describe
 
     C[m, n] = sum_k dec(A[m, k]) * dec(B[n, k])      (C = A . B^T)
 
-evaluated in binary64 with k ascending.  Two implementations:
+evaluated in binary64 with k ascending.  The fp32-weight router GEMM
+(:func:`gemm_f32w`, :func:`gemm_f32w_points`, :func:`gemm_f32w_py`) is the
+same sum with binary32 weights ``W[n, k]`` in place of ``dec(B[n, k])``: the
+PR #48597 page lists an FP32 router GEMM and the preservation of FP32 router
+weights among its parts (section 关联脉络) without printing their code, and
+the reading taken here is the plain product ``C = A . W^T``.  Two
+implementations of each:
 
 * :func:`gemm_f64` / :func:`gemm_points` -- the plain C loop in ``oracle.c``
   (OpenMP over independent columns only), for every size;
@@ -65,6 +71,15 @@ def _load() -> ctypes.CDLL:
                                                ctypes.c_int64, i32p, i32p, ctypes.c_int,
                                                f64p, ctypes.c_int]
         lib.oracle_gemm_f64_points.restype = ctypes.c_int
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_gemm_f32w_f64.argtypes = [u16p, f32p, f64p, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int]
+        lib.oracle_gemm_f32w_f64.restype = ctypes.c_int
+        lib.oracle_gemm_f32w_f64_points.argtypes = [u16p, f32p, ctypes.c_int, ctypes.c_int64,
+                                                    ctypes.c_int64, i32p, i32p, ctypes.c_int,
+                                                    f64p, ctypes.c_int]
+        lib.oracle_gemm_f32w_f64_points.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
@@ -140,6 +155,66 @@ def gemm_points(A_bits: np.ndarray, B_bits: np.ndarray, K: int, ms, ns,
     return out
 
 
+def _as_f32_2d(x: np.ndarray, name: str) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype != np.float32 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D float32 array")
+    return np.ascontiguousarray(x)
+
+
+def gemm_f32w(A_bits: np.ndarray, W: np.ndarray, K: int,
+              threads: Optional[int] = None) -> np.ndarray:
+    """C[M, N] in binary64 from bf16 activations ``A_bits`` [M, lda] (uint16)
+    and binary32 weights ``W`` [N, ldw] (float32); the first ``K`` columns."""
+    A = _as_u16_2d(A_bits, "A_bits")
+    Wc = _as_f32_2d(W, "W")
+    M, lda = A.shape
+    N, ldw = Wc.shape
+    if K < 0 or K > lda or K > ldw:
+        raise ValueError("K must satisfy 0 <= K <= lda, ldw")
+    C = np.zeros((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return C
+    lib = _load()
+    rc = lib.oracle_gemm_f32w_f64(A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                  Wc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                  C.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                  M, N, K, lda, ldw, N, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_f32w_f64 rejected its arguments")
+    return C
+
+
+def gemm_f32w_points(A_bits: np.ndarray, W: np.ndarray, K: int, ms, ns,
+                     threads: Optional[int] = None) -> np.ndarray:
+    """C[ms[i], ns[i]] of :func:`gemm_f32w`, one output at a time."""
+    A = _as_u16_2d(A_bits, "A_bits")
+    Wc = _as_f32_2d(W, "W")
+    ms = np.ascontiguousarray(ms, dtype=np.int32)
+    ns = np.ascontiguousarray(ns, dtype=np.int32)
+    if ms.shape != ns.shape or ms.ndim != 1:
+        raise ValueError("ms and ns must be 1-D and of equal length")
+    if ms.size and (ms.min() < 0 or ms.max() >= A.shape[0] or ns.min() < 0
+                    or ns.max() >= Wc.shape[0]):
+        raise ValueError("sample index out of range")
+    if K < 0 or K > A.shape[1] or K > Wc.shape[1]:
+        raise ValueError("K must satisfy 0 <= K <= lda, ldw")
+    out = np.zeros(ms.size, dtype=np.float64)
+    if ms.size == 0:
+        return out
+    lib = _load()
+    i32p = ctypes.POINTER(ctypes.c_int)
+    rc = lib.oracle_gemm_f32w_f64_points(A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                         Wc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), K,
+                                         A.shape[1], Wc.shape[1], ms.ctypes.data_as(i32p),
+                                         ns.ctypes.data_as(i32p), ms.size,
+                                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                         threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_f32w_f64_points rejected its arguments")
+    return out
+
+
 def bf16_decode(bits) -> np.ndarray:
     """bf16 bit patterns -> binary64 values (exact): the 16 bits are the upper
     half of a binary32 word."""
@@ -177,6 +252,27 @@ def gemm_py(A_bits, B_bits, K: int) -> list:
             s = 0.0
             for k in range(K):
                 s += _dec_py(a_row[k]) * _dec_py(b_row[k])
+            c_row.append(s)
+        C.append(c_row)
+    return C
+
+
+def _f32_py(x) -> float:
+    """A numpy binary32 value as a Python float (exact widening)."""
+    return float(x)
+
+
+def gemm_f32w_py(A_bits, W, K: int) -> list:
+    """Pure-Python loop of :func:`gemm_f32w` for tiny cases."""
+    A = [[int(v) for v in row] for row in np.asarray(A_bits, dtype=np.uint16)]
+    Wr = [[_f32_py(v) for v in row] for row in np.asarray(W, dtype=np.float32)]
+    C = []
+    for a_row in A:
+        c_row = []
+        for w_row in Wr:
+            s = 0.0
+            for k in range(K):
+                s += _dec_py(a_row[k]) * w_row[k]
             c_row.append(s)
         C.append(c_row)
     return C

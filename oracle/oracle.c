@@ -28,6 +28,15 @@
  * decode places the 16 stored bits in the high half of a 32-bit word and
  * reinterprets it (exact; widened to binary64 without rounding).
  *
+ * The same sum with binary32 weights W[n, k] in place of dec(B[n, k])
+ * (oracle_gemm_f32w_f64, oracle_gemm_f32w_f64_points): the router GEMM over
+ * weights kept in fp32.  The PR #48597 page names such a router GEMM, and the
+ * keeping of the router weights in fp32, among the parts of that PR (section
+ * 关联脉络) without printing any of it; the reading taken is the same
+ * product C = A . W^T with W read as binary32.  A bf16 x binary32
+ * product has at most 8 + 24 significant bits, so it is exact in binary64
+ * too, and again only the additions round.
+ *
  * oracle_round_bf16: binary64 -> bf16 round-to-nearest, ties-to-even, via
  * scaling by the quantum of the value's binade and rint().  Used only to
  * predict bf16 outputs in cases where the fp32 result is exact.
@@ -91,6 +100,52 @@ int oracle_gemm_f64_points(const uint16_t *A, const uint16_t *B, int K,
         for (int k = 0; k < K; ++k)
             s += dec_bf16(A[(int64_t)ms[i] * lda + k]) *
                  dec_bf16(B[(int64_t)ns[i] * ldb + k]);
+        out[i] = s;
+    }
+    return 0;
+}
+
+/*
+ * C[m*ldc + n] = sum_k dec(A[m*lda + k]) * W[n*ldw + k] (binary64, k
+ * ascending), W binary32.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_gemm_f32w_f64(const uint16_t *A, const float *W, double *C,
+                         int M, int N, int K, int64_t lda, int64_t ldw,
+                         int64_t ldc, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldw < K || ldc < N)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int n = 0; n < N; ++n) {
+        for (int m = 0; m < M; ++m) {
+            double s = 0.0;
+            for (int k = 0; k < K; ++k)
+                s += dec_bf16(A[(int64_t)m * lda + k]) *
+                     (double)W[(int64_t)n * ldw + k];
+            C[(int64_t)m * ldc + n] = s;
+        }
+    }
+    return 0;
+}
+
+/* The same for an explicit list of (m, n) pairs: out[i] = C[ms[i], ns[i]]. */
+int oracle_gemm_f32w_f64_points(const uint16_t *A, const float *W, int K,
+                                int64_t lda, int64_t ldw, const int *ms,
+                                const int *ns, int npts, double *out,
+                                int nthreads)
+{
+    if (K < 0 || lda < K || ldw < K || npts < 0)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int i = 0; i < npts; ++i) {
+        double s = 0.0;
+        for (int k = 0; k < K; ++k)
+            s += dec_bf16(A[(int64_t)ms[i] * lda + k]) *
+                 (double)W[(int64_t)ns[i] * ldw + k];
         out[i] = s;
     }
     return 0;

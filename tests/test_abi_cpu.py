@@ -63,8 +63,10 @@ def test_dispatch_valid_on_a_shape_grid():
             for N in (1, 3, 16, 128, 129, 2112, 24576):
                 cfg = skg.skinny_gemm_dispatch(M, K, N)
                 assert skg.skinny_gemm_check_config(M, K, N, cfg), (M, K, N, cfg)
-                assert (cfg.backend in (skg.SKG_BACKEND_DOT, skg.SKG_BACKEND_EVEN)) == \
-                    (cfg.split_k == 1)
+                if cfg.backend == skg.SKG_BACKEND_DOT:
+                    assert cfg.split_k == 1
+                elif cfg.backend != skg.SKG_BACKEND_EVEN:
+                    assert cfg.split_k >= 2
 
 
 def test_dispatch_rejects():
@@ -106,8 +108,8 @@ def test_check_config_rules():
 
 
 def test_even_backend_rules():
-    """SKG_BACKEND_EVEN: no K split; min(N, 256 x rb_per_wg) workgroups of
-    floor/ceil(N / G) rows, which the waves must cover; no workspace."""
+    """SKG_BACKEND_EVEN without a K split: min(N, 256 x rb_per_wg) workgroups
+    of floor/ceil(N / G) rows, which the waves must cover; no workspace."""
     mk = _capi.SkgConfig.make
     ev = dict(backend=skg.SKG_BACKEND_EVEN, split_k=1, waves_k=2, depth=4)
     # 2112 rows over 256 workgroups: up to 9 rows, 12 covered by 3 VALU waves
@@ -129,12 +131,46 @@ def test_even_backend_rules():
     # fewer rows than workgroups: one row each
     assert skg.skinny_gemm_check_config(
         1, 64, 100, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=1, rb_per_wg=1, **ev))
-    # no K split, and at most 64 workgroups per CU
-    assert not skg.skinny_gemm_check_config(
-        2, 7168, 2112, mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_VALU, split_k=2,
-                          row_tiles=1, waves_n=3, waves_k=2, depth=4))
+    # at most 64 workgroups per CU
     assert not skg.skinny_gemm_check_config(
         2, 7168, 2112, mk(inner=skg.SKG_INNER_VALU, row_tiles=1, waves_n=3, rb_per_wg=65, **ev))
+
+
+def test_even_backend_with_k_split():
+    """SKG_BACKEND_EVEN with split_k = S: 256 x rb_per_wg workgroups are
+    256 x rb_per_wg / S row blocks times S K slices (S must divide the
+    workgroup count); each row block holds floor/ceil(N / blocks) rows; the
+    partials go through the workspace and a ticket per row block."""
+    mk = _capi.SkgConfig.make
+    lib = _capi.lib()
+
+    def geom(M, K, N, cfg):
+        st = lib.skinny_gemm_check_config(M, K, N, ctypes.byref(cfg))
+        return st == 0
+
+    # 7168 rows, split 2: 128 row blocks of 56 rows; 64-row MFMA waves cover them
+    c = mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_MFMA_RING_GA, split_k=2,
+           row_tiles=4, waves_n=1, waves_k=2, depth=2, rb_per_wg=1)
+    assert geom(16, 14336, 7168, c)
+    # partials [128 blocks][2 slices][16 tokens][64 rows] fp32 + 128 tickets
+    assert skg.skinny_gemm_workspace_bytes(16, 14336, 7168, c) == 128 * 2 * 16 * 64 * 4 + 128 * 4
+    # 32 rows cannot hold 56
+    assert not geom(16, 14336, 7168, mk(backend=skg.SKG_BACKEND_EVEN,
+                                        inner=skg.SKG_INNER_MFMA_RING_GA, split_k=2, row_tiles=2,
+                                        waves_n=1, waves_k=2, depth=3, rb_per_wg=1))
+    # split 4 of 2112 rows: 64 blocks of 33 rows, 3 MFMA waves of 16 rows
+    assert geom(16, 7168, 2112, mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_MFMA_GA,
+                                   split_k=4, row_tiles=1, waves_n=3, waves_k=1, depth=4,
+                                   rb_per_wg=1))
+    # the split must divide 256 x rb_per_wg
+    for S, rpw, ok in ((3, 1, False), (3, 3, True), (5, 1, False), (8, 1, True), (128, 1, False)):
+        cfg = mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_VALU_GA, split_k=S,
+                 row_tiles=4, waves_n=8, waves_k=1, depth=2, rb_per_wg=rpw)
+        assert geom(2, 7168, 2048, cfg) == ok, (S, rpw)
+    # a K too short for the slices (empty last slice) is rejected
+    assert not geom(2, 64, 2048, mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_VALU_GA,
+                                    split_k=8, row_tiles=4, waves_n=8, waves_k=1, depth=2,
+                                    rb_per_wg=1))
 
 
 def test_lds_ring_sizes():

@@ -51,7 +51,12 @@ def test_split_k_forced_is_reproducible():
              (16, MK(inner=skg.SKG_INNER_VALU, split_k=7, row_tiles=1, waves_n=1, waves_k=2,
                      depth=4)),
              (8, MK(inner=skg.SKG_INNER_VALU_GA, split_k=3, row_tiles=2, waves_n=1, waves_k=2,
-                    depth=2))]
+                    depth=2)),
+             # rows dealt evenly to 64 row blocks x 4 K slices
+             (16, MK(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_MFMA_RING_GA, split_k=4,
+                     row_tiles=1, waves_n=1, waves_k=2, depth=2)),
+             (4, MK(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_VALU, split_k=2,
+                    row_tiles=1, waves_n=1, waves_k=1, depth=4))]
     for M, cfg in cases:
         A, B = _problem(M, 7168, 256)
         ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))

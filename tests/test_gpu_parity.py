@@ -65,7 +65,10 @@ def _configs():
                 MK(inner=VG, split_k=3, row_tiles=R, waves_n=1, waves_k=2, depth=PF, rb_per_wg=2),
                 MK(backend=P2, inner=VG, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF),
                 MK(backend=EV, inner=V, split_k=1, row_tiles=R, waves_n=2, waves_k=2, depth=PF),
-                MK(backend=EV, inner=VG, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF)]
+                MK(backend=EV, inner=VG, split_k=1, row_tiles=R, waves_n=1, waves_k=1, depth=PF),
+                MK(backend=EV, inner=V, split_k=2, row_tiles=R, waves_n=2, waves_k=1, depth=PF),
+                MK(backend=EV, inner=VG, split_k=4, row_tiles=R, waves_n=1, waves_k=2, depth=PF,
+                   rb_per_wg=3)]
     for (G, PF) in skg._capi.MFMA_VARIANTS:
         out += [MK(inner=F, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 # 8 waves of 4 transpose tiles each would not leave LDS for A
@@ -84,7 +87,11 @@ def _configs():
                 MK(backend=P2, inner=RG, split_k=2, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 MK(backend=EV, inner=GA, split_k=1, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
                 MK(backend=EV, inner=F, split_k=1, row_tiles=G, waves_n=2, waves_k=1, depth=PF),
-                MK(backend=EV, inner=RG, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF)]
+                MK(backend=EV, inner=RG, split_k=1, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(backend=EV, inner=GA, split_k=2, row_tiles=G, waves_n=1, waves_k=2, depth=PF),
+                MK(backend=EV, inner=RG, split_k=4, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
+                MK(backend=EV, inner=RF, split_k=4, row_tiles=G, waves_n=1, waves_k=1, depth=PF,
+                   rb_per_wg=2)]
     return out
 
 

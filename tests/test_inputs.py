@@ -45,3 +45,14 @@ def test_workload_points():
     assert len(pts) == 29
     assert sum(1 for p in pts if p["out"] == "bf16") == 14
     assert all(p["M"] <= 16 for p in pts)
+
+
+def test_f32_weights_are_the_unrounded_draws():
+    from latency_decode_gemm_amd import inputs
+    W = inputs.make_w_f32(100, 7, ldw=104)
+    B = inputs.make_b(100, 7, ldb=104)
+    assert W.dtype == np.float32 and W.shape == (7, 104)
+    assert np.array_equal(inputs.f32_to_bf16_bits(W[:, :100]), B[:, :100])
+    assert np.isnan(W[:, 100:]).all()
+    # the draws use every bit of the binary32 significand
+    assert (W[:, :100].view(np.uint32) & 0xFFFF).any()
