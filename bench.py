@@ -18,7 +18,10 @@ Prints ONE JSON line:
                  its dispatches record (skinny_gemm_bf16_timed) on every step
                  of the timed region;
   cpu_baseline = the CPU oracle timed on this host over the same workload.
-``--points-out FILE`` also writes, for every one of the 29 workload points,
+``--workload router_f32w`` measures the router GEMM over fp32 weights
+(skinny_gemm_f32w; weight bytes 4*N*K) the same way.
+``--points-out FILE`` also writes, for every one of the 29 workload points
+and the 12 fp32-weight router points,
 the kernel time per call (median of 200 dispatch-recorded event pairs), the
 time per call eager, from HIP-graph replay and with one hot weight copy, the
 streaming-read ceiling for the same weight bytes, and the CPU oracle on all
@@ -50,6 +53,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # taken with is stored beside them and compared separately)
 KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
                   "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_api.cpp"]
+F32W_SUFFIX = "_w32"  # point names of the fp32-weight router GEMM
 
 
 def kernel_source_hash() -> str:
@@ -79,42 +83,54 @@ def parse():
 
 
 class Point:
-    """Device buffers of one workload point (A, rotating B copies, C)."""
+    """Device buffers of one workload point (A, rotating B copies, C); a point
+    with ``w == "f32"`` runs the fp32-weight entry points."""
 
     def __init__(self, torch, skg, inputs, p, b_pool):
         self.M, self.K, self.N = p["M"], p["K"], p["N"]
+        self.f32w = p.get("w") == "f32"
+        wsz = 4 if self.f32w else 2
         self.out = p["out"]
         self.ldc = p["ldc"] or self.N
         self.A_bits = inputs.make_a(self.M, self.K, self.N)
         self.A = torch.from_numpy(self.A_bits.view("int16")).cuda().view(torch.bfloat16)
-        self.copies = b_pool[(self.K, self.N)]
+        self.copies = b_pool[(self.K, self.N, self.f32w)]
         dt = torch.bfloat16 if self.out == "bf16" else torch.float32
         self.Cbuf = torch.zeros((self.M, self.ldc), dtype=dt, device="cuda")
         self.odt = skg.SKG_OUT_BF16 if self.out == "bf16" else skg.SKG_OUT_F32
-        self.cfg = skg.skinny_gemm_dispatch(self.M, self.K, self.N)
+        dispatch = skg.skinny_gemm_f32w_dispatch if self.f32w else skg.skinny_gemm_dispatch
+        self.cfg = dispatch(self.M, self.K, self.N)
         self.s_out = 2 if self.out == "bf16" else 4
-        self.weight_bytes = 2 * self.N * self.K
-        self.alg_bytes = 2 * self.N * self.K + 2 * self.M * self.K + self.M * self.N * self.s_out
+        self.weight_bytes = wsz * self.N * self.K
+        self.alg_bytes = self.weight_bytes + 2 * self.M * self.K + self.M * self.N * self.s_out
+
+    def key(self):
+        return (self.K, self.N, self.f32w)
 
     def name(self):
         return f"M{self.M}_K{self.K}_N{self.N}_{self.out}" + (
-            f"_ldc{self.ldc}" if self.ldc != self.N else "")
+            f"_ldc{self.ldc}" if self.ldc != self.N else "") + (F32W_SUFFIX if self.f32w else "")
 
 
 class BPool:
-    """Per (K, N): the seeded weights and byte-identical copies of them."""
+    """Per (K, N, fp32 weights?): the seeded weights (bf16 bits, or float32)
+    and byte-identical copies of them on the device."""
 
     def __init__(self, torch, inputs, shapes, rotate_bytes=ROTATE_BYTES):
         self.torch = torch
         self.bits = {}
         self.copies = {}
-        for (K, N) in shapes:
-            bits = inputs.make_b(K, N)
-            self.bits[(K, N)] = bits
-            base = torch.from_numpy(bits.view("int16")).cuda().view(torch.bfloat16)
-            n = max(2, math.ceil(rotate_bytes / (2 * N * K)))
+        for (K, N, f32w) in shapes:
+            if f32w:
+                bits = inputs.make_w_f32(K, N)
+                base = torch.from_numpy(bits).cuda()
+            else:
+                bits = inputs.make_b(K, N)
+                base = torch.from_numpy(bits.view("int16")).cuda().view(torch.bfloat16)
+            self.bits[(K, N, f32w)] = bits
+            n = max(2, math.ceil(rotate_bytes / (base.element_size() * N * K)))
             lst = [base] + [base.clone() for _ in range(n - 1)]
-            self.copies[(K, N)] = {"list": lst, "next": 0}
+            self.copies[(K, N, f32w)] = {"list": lst, "next": 0}
 
     def __getitem__(self, key):
         return self.copies[key]
@@ -122,14 +138,15 @@ class BPool:
 
 def call(lib, pt, B, stream_handle, events=None):
     if events is None:
-        st = lib.skinny_gemm_bf16(pt.A.data_ptr(), B.data_ptr(), pt.Cbuf.data_ptr(), pt.M, pt.N,
-                                  pt.K, pt.K, pt.K, pt.ldc, pt.odt, stream_handle)
+        fn = lib.skinny_gemm_f32w if pt.f32w else lib.skinny_gemm_bf16
+        st = fn(pt.A.data_ptr(), B.data_ptr(), pt.Cbuf.data_ptr(), pt.M, pt.N, pt.K, pt.K, pt.K,
+                pt.ldc, pt.odt, stream_handle)
     else:
-        st = lib.skinny_gemm_bf16_timed(pt.A.data_ptr(), B.data_ptr(), pt.Cbuf.data_ptr(), pt.M,
-                                        pt.N, pt.K, pt.K, pt.K, pt.ldc, pt.odt, stream_handle,
-                                        events[0].handle, events[1].handle)
+        fn = lib.skinny_gemm_f32w_timed if pt.f32w else lib.skinny_gemm_bf16_timed
+        st = fn(pt.A.data_ptr(), B.data_ptr(), pt.Cbuf.data_ptr(), pt.M, pt.N, pt.K, pt.K, pt.K,
+                pt.ldc, pt.odt, stream_handle, events[0].handle, events[1].handle)
     if st != 0:
-        raise RuntimeError(f"skinny_gemm_bf16 failed for {pt.name()}: status {st}")
+        raise RuntimeError(f"skinny_gemm call failed for {pt.name()}: status {st}")
 
 
 def next_copy(pt):
@@ -147,9 +164,13 @@ def check_parity(oracle, acceptance, pt, bits_B, torch):
     ns = np.sort(rng.choice(pt.N, size=min(64, pt.N), replace=False))
     ms = np.repeat(np.arange(pt.M), ns.size)
     nn = np.tile(ns, pt.M)
-    ref = oracle.gemm_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
     an = acceptance.row_norms(oracle.bf16_decode(pt.A_bits), pt.K)
-    bn = acceptance.row_norms(oracle.bf16_decode(bits_B[ns]), pt.K)
+    if pt.f32w:
+        ref = oracle.gemm_f32w_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
+        bn = acceptance.row_norms(bits_B[ns].astype(np.float64), pt.K)
+    else:
+        ref = oracle.gemm_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
+        bn = acceptance.row_norms(oracle.bf16_decode(bits_B[ns]), pt.K)
     return acceptance.assess(C[:, ns], ref, an, bn, pt.out)
 
 
@@ -218,7 +239,7 @@ def cpu_baseline(oracle, pts, bpool, budget_s):
     while passes == 0 or t_total < budget_s:
         for pt in pts:
             t0 = time.perf_counter()
-            oracle.gemm_f64(pt.A_bits, bpool.bits[(pt.K, pt.N)], pt.K, threads=threads)
+            oracle_gemm(oracle, pt)(pt.A_bits, bpool.bits[pt.key()], pt.K, threads=threads)
             t_total += time.perf_counter() - t0
             bytes_total += pt.weight_bytes
         passes += 1
@@ -227,6 +248,10 @@ def cpu_baseline(oracle, pts, bpool, budget_s):
             "sample": f"the whole workload ({len(pts)} calls, every output), {passes} pass(es), "
                       f"{t_total:.1f} s; binary64 C loop, OpenMP over columns; "
                       f"{threads} threads of {os.cpu_count()} logical CPUs, {cpu_model()}"}
+
+
+def oracle_gemm(oracle, pt):
+    return oracle.gemm_f32w if pt.f32w else oracle.gemm_f64
 
 
 def oracle_mod():
@@ -249,16 +274,21 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
     zero-fill kernel) that marks them in a kernel trace, so a rocprofv3
     kernel trace of this run can be attributed to points by order."""
     h = stream.cuda_stream
-    spec = inputs.all_points()
-    shapes = list(dict.fromkeys((p["K"], p["N"]) for p in spec))
+    spec = inputs.all_points() + inputs.WORKLOADS_F32W["router_f32w"]
+
+    def key_of(p):
+        return (p["K"], p["N"], p.get("w") == "f32")
+
+    shapes = list(dict.fromkeys(key_of(p) for p in spec))
     table = {}
     order = 0
     sink = torch.zeros(512, dtype=torch.int32, device="cuda")
-    for (K, N) in shapes:
-        sub = [p for p in spec if (p["K"], p["N"]) == (K, N)]
-        bp = BPool(torch, inputs, [(K, N)])
+    for (K, N, f32w) in shapes:
+        sub = [p for p in spec if key_of(p) == (K, N, f32w)]
+        bp = BPool(torch, inputs, [(K, N, f32w)])
         ps = [Point(torch, skg, inputs, p, bp) for p in sub]
-        skg.skinny_gemm_warmup([(K, N)], [p.M for p in ps], stream=stream)
+        warm_fn = skg.skinny_gemm_f32w_warmup if f32w else skg.skinny_gemm_warmup
+        warm_fn([(K, N)], [p.M for p in ps], stream=stream)
         ev = [(skg.HipEvent(), skg.HipEvent()) for _ in range(calls)]
         for pt in ps:
             st = lib.skinny_gemm_bf16(pt.A.data_ptr(), pt.A.data_ptr(), pt.Cbuf.data_ptr(), pt.M,
@@ -275,6 +305,7 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
                 "M": pt.M, "K": pt.K, "N": pt.N, "out": pt.out, "ldc": pt.ldc,
                 "config": pt.cfg.as_dict(), "trace_order": order, "trace_warm": warm,
                 "trace_calls": calls,
+                "weights": "f32" if pt.f32w else "bf16",
                 "dispatches_per_call": 2 if pt.cfg.backend == skg.SKG_BACKEND_SPLITK_2PASS else 1,
                 "kernel_us_events_median": round(median(ev_us), 3),
                 "weight_bytes": pt.weight_bytes, "alg_bytes": pt.alg_bytes}
@@ -282,8 +313,8 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
         eager = time_points_eager(torch, lib, ps, stream)
         graph = time_points_graph(torch, lib, ps, stream)
         # streaming-read ceiling over the same rotating weight copies
-        lst = bp[(K, N)]["list"]
-        nb = 2 * N * K
+        lst = bp[(K, N, f32w)]["list"]
+        nb = lst[0].element_size() * N * K
         for i in range(4):
             lib.skinny_gemm_stream_read(lst[i % len(lst)].data_ptr(), nb, sink.data_ptr(), h)
         torch.cuda.synchronize()
@@ -295,9 +326,9 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
             e1.record()
         torch.cuda.synchronize()
         read_us = e0.elapsed_time(e1) * 1000.0 / calls
-        hot = BPool(torch, inputs, [(K, N)], rotate_bytes=0)
+        hot = BPool(torch, inputs, [(K, N, f32w)], rotate_bytes=0)
         for p in ps:
-            p.copies = hot[(K, N)]
+            p.copies = hot[(K, N, f32w)]
             p.copies["list"] = p.copies["list"][:1]
         hot_us = time_points_graph(torch, lib, ps, stream)
         for pt in ps:
@@ -310,12 +341,12 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
             e["weight_GBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3, 1)
             e["frac_of_8TBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3 / PEAK_HBM_GBS, 4)
             # CPU oracle on this point
-            bits_B = bp.bits[(K, N)]
+            bits_B = bp.bits[(K, N, f32w)]
             for threads, key in ((oracle.default_threads(), "cpu_all_cores"), (1, "cpu_one_core")):
                 ts = []
                 for rep in range(4):
                     t0 = time.perf_counter()
-                    oracle.gemm_f64(pt.A_bits, bits_B, K, threads=threads)
+                    oracle_gemm(oracle, pt)(pt.A_bits, bits_B, K, threads=threads)
                     ts.append(time.perf_counter() - t0)
                 e[key] = {"us_per_call": round(median(ts[1:]) * 1e6, 1), "threads": threads}
         del ps, bp, hot
@@ -359,19 +390,22 @@ def main():
         print("bench.py: libskinny_gemm.so has no gfx950 device/code to run", file=sys.stderr)
         sys.exit(1)
 
-    workload = inputs.WORKLOADS[args.workload]
+    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_F32W)
+    workload = groups[args.workload]
     if args.only:
         M, K, N = (int(x) for x in args.only.split(","))
         workload = [p for p in inputs.all_points() if (p["M"], p["K"], p["N"]) == (M, K, N)]
-    shapes = list(dict.fromkeys((p["K"], p["N"]) for p in workload))
-    ms = sorted(set(p["M"] for p in workload))
+    shapes = list(dict.fromkeys((p["K"], p["N"], p.get("w") == "f32") for p in workload))
     bpool = BPool(torch, inputs, shapes)
     pts = [Point(torch, skg, inputs, p, bpool) for p in workload]
     # all work on one non-default stream (graph capture needs one)
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     h = stream.cuda_stream
-    skg.skinny_gemm_warmup(shapes, ms, stream=stream)
+    for (K, N, f32w) in shapes:
+        ms = sorted(set(p.M for p in pts if p.key() == (K, N, f32w)))
+        warm_fn = skg.skinny_gemm_f32w_warmup if f32w else skg.skinny_gemm_warmup
+        warm_fn([(K, N)], ms, stream=stream)
 
     # untimed warm-up steps; also find the dominant point (largest time per call)
     for _ in range(max(args.warmup, 1)):
@@ -414,7 +448,7 @@ def main():
         import oracle
         from oracle import acceptance
         for pt in pts:
-            r = check_parity(oracle, acceptance, pt, bpool.bits[(pt.K, pt.N)], torch)
+            r = check_parity(oracle, acceptance, pt, bpool.bits[pt.key()], torch)
             if not r["ok"]:
                 bad.append((pt.name(), r))
     if bad:
@@ -445,7 +479,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if any(p.f32w for p in pts) else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload + ": " + ", ".join(p.name() for p in pts),
                    "accumulate": "f32", "weight_bytes_per_step": weight_bytes_step,

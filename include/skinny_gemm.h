@@ -196,6 +196,53 @@ int skinny_gemm_warmup_keys(const int *kn_pairs, int n_shapes,
 int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values,
                        int n_m, void *stream, int *n_configs_out);
 
+/*
+ * The router GEMM over fp32 weights: C[m, n] = sum_k A[m, k] * W[n, k] with
+ * A bf16 and W fp32 (each product one fp32 fused multiply-add of the widened
+ * activation, fp32 accumulation).  The PR #48597 page ("GLM-5.2 Blackwell
+ * decode optimizations", section 关联脉络) names a router GEMM over fp32
+ * weights, and the keeping of router weights in fp32, among that PR's parts;
+ * the PR #42562 page (section 风险与影响) notes that its bf16 kernel leaves
+ * fp32 weights to other paths.  Same conventions as the bf16 entry points,
+ * except:
+ *   W: device fp32 [N, ldw], 16-byte aligned, ldw % 4 == 0, ldw >= K
+ *      (else SKG_ERR_MISALIGNED / SKG_ERR_INVALID_ARG).
+ * Only the VALU inner products (SKG_INNER_VALU, SKG_INNER_VALU_GA) take fp32
+ * weights; every backend does.  The configurations come from a table of
+ * their own (skinny_gemm_f32w_dispatch).
+ */
+int skinny_gemm_f32w(const void *A, const void *W, void *C, int M, int N, int K,
+                     int64_t lda, int64_t ldw, int64_t ldc, int out_dtype, void *stream);
+
+/* skinny_gemm_f32w with kernel start/end recorded into caller events, as
+ * skinny_gemm_bf16_timed does. */
+int skinny_gemm_f32w_timed(const void *A, const void *W, void *C, int M, int N, int K,
+                           int64_t lda, int64_t ldw, int64_t ldc, int out_dtype,
+                           void *stream, void *start_event, void *stop_event);
+
+/* skinny_gemm_f32w with an explicit configuration (tests, tuning); a
+ * configuration that cannot run over fp32 weights returns SKG_ERR_INVALID_ARG. */
+int skinny_gemm_f32w_with_config(const void *A, const void *W, void *C, int M,
+                                 int N, int K, int64_t lda, int64_t ldw,
+                                 int64_t ldc, int out_dtype, void *stream,
+                                 const skg_config *cfg);
+
+/* The configuration skinny_gemm_f32w uses for (M, K, N); pure host, as
+ * skinny_gemm_dispatch. */
+int skinny_gemm_f32w_dispatch(int M, int K, int N, skg_config *out);
+
+/* Whether cfg can run (M, K, N) over fp32 weights; pure host. */
+int skinny_gemm_f32w_check_config(int M, int K, int N, const skg_config *cfg);
+
+/* Warm-up keys and warm-up for fp32 weights, as skinny_gemm_warmup_keys and
+ * skinny_gemm_warmup (the same arguments and behaviour, over
+ * skinny_gemm_f32w_dispatch). */
+int skinny_gemm_f32w_warmup_keys(const int *kn_pairs, int n_shapes,
+                                 const int *m_values, int n_m, skg_config *out,
+                                 int capacity, int *n_out);
+int skinny_gemm_f32w_warmup(const int *kn_pairs, int n_shapes, const int *m_values,
+                            int n_m, void *stream, int *n_configs_out);
+
 /* 1 if a gfx950 device is current and the library's kernels load, else 0. */
 int skinny_gemm_available(void);
 

@@ -11,7 +11,10 @@ from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_EVEN, SKG_BACKEND_SPLITK, SKG_B
                     SKG_INNER_VALU_GA, SKG_MAX_M, SKG_OK,
                     SKG_OUT_BF16, SKG_OUT_F32, HipEvent, SkgConfig, SkinnyGemmError)
 from .ops import (skinny_gemm_available, skinny_gemm_bf16, skinny_gemm_bf16_timed,
-                  skinny_gemm_bf16_with_config,
+                  skinny_gemm_bf16_with_config, skinny_gemm_f32w, skinny_gemm_f32w_check_config,
+                  skinny_gemm_f32w_dispatch, skinny_gemm_f32w_timed,
+                  skinny_gemm_f32w_warmup, skinny_gemm_f32w_warmup_keys,
+                  skinny_gemm_f32w_with_config,
                   skinny_gemm_check_config, skinny_gemm_dispatch, skinny_gemm_stream_read,
                   skinny_gemm_strerror,
                   skinny_gemm_warmup, skinny_gemm_warmup_keys, skinny_gemm_workspace_bytes)

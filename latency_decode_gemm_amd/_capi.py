@@ -93,6 +93,15 @@ SIGNATURES = {
     "skinny_gemm_workspace_bytes": (_i, [_i, _i, _i, _cfgp, ctypes.POINTER(ctypes.c_size_t)]),
     "skinny_gemm_warmup_keys": (_i, [_ip, _i, _ip, _i, _cfgp, _i, _ip]),
     "skinny_gemm_warmup": (_i, [_ip, _i, _ip, _i, _vp, _ip]),
+    "skinny_gemm_f32w": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp]),
+    "skinny_gemm_f32w_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp,
+                                    _vp, _vp]),
+    "skinny_gemm_f32w_with_config": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i,
+                                          _vp, _cfgp]),
+    "skinny_gemm_f32w_dispatch": (_i, [_i, _i, _i, _cfgp]),
+    "skinny_gemm_f32w_check_config": (_i, [_i, _i, _i, _cfgp]),
+    "skinny_gemm_f32w_warmup_keys": (_i, [_ip, _i, _ip, _i, _cfgp, _i, _ip]),
+    "skinny_gemm_f32w_warmup": (_i, [_ip, _i, _ip, _i, _vp, _ip]),
     "skinny_gemm_available": (_i, []),
     "skinny_gemm_stream_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
     "skinny_gemm_strerror": (ctypes.c_char_p, [_i]),

@@ -36,8 +36,11 @@ struct TableEntry {
 };
 
 #include "tuned_table.inc"
+#include "tuned_table_f32w.inc"
 
 constexpr int kNumTable = sizeof(kTunedTable) / sizeof(kTunedTable[0]);
+constexpr int kNumTableF32w = sizeof(kTunedTableF32w) / sizeof(kTunedTableF32w[0]);
+
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 int round_up(int a, int b) { return ceil_div(a, b) * b; }
@@ -48,14 +51,15 @@ bool config_equal(const skg_config &a, const skg_config &b) {
            a.depth == b.depth && a.rb_per_wg == b.rb_per_wg;
 }
 
-// Default for shapes the table does not list: VALU up to M = 8, MFMA above;
-// 4 waves per workgroup (2 on rows x 2 on K); K split only when the staged A
-// slice would exceed 64 KB or the row blocks cannot cover the 256 CUs; each
-// workgroup then streams enough row blocks to keep the grid near 512.
-skg_config default_config(int M, int K, int N) {
+// Default for shapes the table does not list: VALU up to M = 8, MFMA above
+// (fp32 weights: VALU throughout); 4 waves per workgroup (2 on rows x 2 on
+// K); K split only when the staged A slice would exceed 64 KB or the row
+// blocks cannot cover the 256 CUs; each workgroup then streams enough row
+// blocks to keep the grid near 512.
+skg_config default_config(int M, int K, int N, bool f32w = false) {
     skg_config c;
     std::memset(&c, 0, sizeof c);
-    c.inner = (M > 8) ? SKG_INNER_MFMA_GA : SKG_INNER_VALU;
+    c.inner = (M > 8 && !f32w) ? SKG_INNER_MFMA_GA : SKG_INNER_VALU;
     c.row_tiles = (c.inner == SKG_INNER_VALU) ? 2 : 1;
     c.depth = 4;
     c.waves_n = 2;
@@ -135,8 +139,10 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
     return SKG_OK;
 }
 
+// Argument checks; f32w: B holds fp32 weights (rows of ldb elements, a
+// multiple of 4 so that every row starts 16-byte aligned).
 int check_args(const void *A, const void *B, const void *C, int M, int N, int K, int64_t lda,
-               int64_t ldb, int64_t ldc, int out_dtype) {
+               int64_t ldb, int64_t ldc, int out_dtype, bool f32w = false) {
     if (M < 0 || N < 0 || K < 0) return SKG_ERR_INVALID_ARG;
     if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
     if (out_dtype != SKG_OUT_F32 && out_dtype != SKG_OUT_BF16) return SKG_ERR_INVALID_ARG;
@@ -147,7 +153,7 @@ int check_args(const void *A, const void *B, const void *C, int M, int N, int K,
     if (K > 0) {
         if ((reinterpret_cast<uintptr_t>(A) & 15u) || (reinterpret_cast<uintptr_t>(B) & 15u))
             return SKG_ERR_MISALIGNED;
-        if ((lda & 7) || (ldb & 7)) return SKG_ERR_MISALIGNED;
+        if ((lda & 7) || (ldb & (f32w ? 3 : 7))) return SKG_ERR_MISALIGNED;
     }
     const uintptr_t csz = (out_dtype == SKG_OUT_F32) ? 4u : 2u;
     if (reinterpret_cast<uintptr_t>(C) & (csz - 1)) return SKG_ERR_MISALIGNED;
@@ -156,7 +162,7 @@ int check_args(const void *A, const void *B, const void *C, int M, int N, int K,
 
 int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda, int64_t ldb,
         int64_t ldc, int out_dtype, void *stream_v, const skg_config &cfg,
-        void *start_v = nullptr, void *stop_v = nullptr) {
+        void *start_v = nullptr, void *stop_v = nullptr, bool f32w = false) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     hipEvent_t start = reinterpret_cast<hipEvent_t>(start_v);
     hipEvent_t stop = reinterpret_cast<hipEvent_t>(stop_v);
@@ -178,10 +184,13 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.N = N;
     p.K = K;
     p.out_bf16 = (out_dtype == SKG_OUT_BF16);
+    p.w_f32 = f32w ? 1 : 0;
     if (K < kChunk)  // rows shorter than one 16-byte window
         return launch_small_k(p, stream, start, stop) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
     Geometry g;
     if (!make_geometry(M, K, N, cfg, &g)) return SKG_ERR_INVALID_ARG;
+    if (f32w && !variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, true, M))
+        return SKG_ERR_INVALID_ARG;
     p.nck = g.nck;
     p.nfull = g.nfull;
     p.split_k = cfg.split_k;
@@ -295,30 +304,153 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
 
 using namespace skg;
 
-extern "C" {
+namespace {
 
-int skinny_gemm_dispatch(int M, int K, int N, skg_config *out) {
+// Whether cfg can run (M, K, N) over bf16 (f32w false) or fp32 weights.
+bool config_ok(int M, int K, int N, const skg_config &cfg, bool f32w) {
+    Geometry g;
+    if (!make_geometry(M, K, N, cfg, &g)) return false;
+    return !f32w || variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, true, M);
+}
+
+// The tuned entry for (M, K, N), else the default rule; pure.
+int dispatch_impl(int M, int K, int N, bool f32w, skg_config *out) {
     if (!out) return SKG_ERR_INVALID_ARG;
     if (M < 1 || K < 0 || N < 1) return M > SKG_MAX_M ? SKG_ERR_UNSUPPORTED : SKG_ERR_INVALID_ARG;
     if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
-    for (int i = 0; i < kNumTable; ++i) {
-        const TableEntry &e = kTunedTable[i];
-        if (e.M == M && e.K == K && e.N == N) {
+    const TableEntry *table = f32w ? kTunedTableF32w : kTunedTable;
+    const int n = f32w ? kNumTableF32w : kNumTable;
+    for (int i = 0; i < n; ++i) {
+        const TableEntry &e = table[i];
+        if (e.M == M && e.K == K && e.N == N && config_ok(M, K, N, e.cfg, f32w)) {
+            *out = e.cfg;
+            return SKG_OK;
+        }
+    }
+    *out = default_config(M, K, N, f32w);
+    return SKG_OK;
+}
+
+// Warm-up keys and warm-up over bf16 (f32w false) or fp32 weights.
+int warmup_keys_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
+                     skg_config *out, int capacity, int *n_out) {
+    if (n_shapes < 0 || n_m < 0 || capacity < 0 || !n_out) return SKG_ERR_INVALID_ARG;
+    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values) || (capacity > 0 && !out))
+        return SKG_ERR_INVALID_ARG;
+    std::vector<skg_config> keys;
+    for (int i = 0; i < n_shapes; ++i) {
+        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
+        for (int j = 0; j < n_m; ++j) {
+            skg_config c;
+            const int st = dispatch_impl(m_values[j], K, N, f32w, &c);
+            if (st != SKG_OK) return st;
+            bool seen = false;
+            for (const skg_config &k : keys) seen = seen || config_equal(k, c);
+            if (!seen) keys.push_back(c);
+        }
+    }
+    for (int i = 0; i < (int)keys.size() && i < capacity; ++i) out[i] = keys[i];
+    *n_out = (int)keys.size();
+    return SKG_OK;
+}
+
+int warmup_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
+                void *stream_v, int *n_configs_out) {
+    if (n_shapes < 0 || n_m < 0) return SKG_ERR_INVALID_ARG;
+    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values)) return SKG_ERR_INVALID_ARG;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    // the distinct configurations, the workspace they need, and a scratch
+    // problem large enough to run each of them once
+    std::vector<std::pair<skg_config, std::pair<int, int>>> todo;  // cfg, (M, K)
+    size_t need_f = 0, need_t = 0, max_a = 0, max_b = 0, max_c = 0;
+    for (int i = 0; i < n_shapes; ++i) {
+        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
+        if (K < 0 || N < 1) return SKG_ERR_INVALID_ARG;
+        for (int j = 0; j < n_m; ++j) {
+            const int M = m_values[j];
+            skg_config c;
+            const int st = dispatch_impl(M, K, N, f32w, &c);
+            if (st != SKG_OK) return st;
+            if (K == 0) continue;
             Geometry g;
-            if (make_geometry(M, K, N, e.cfg, &g)) {
-                *out = e.cfg;
-                return SKG_OK;
+            if (!make_geometry(M, K, N, c, &g)) return SKG_ERR_INVALID_ARG;
+            need_f = std::max(need_f, g.ws_floats);
+            need_t = std::max(need_t, g.n_tickets);
+            bool seen = false;
+            for (auto &t : todo)
+                seen = seen || (config_equal(t.first, c) && t.second.first == M &&
+                                t.second.second == K);
+            if (!seen) {
+                todo.push_back({c, {M, K}});
+                const size_t rows = (size_t)g.rows_per_wg;
+                const size_t ld = (size_t)round_up(K, kChunk);
+                max_a = std::max(max_a, (size_t)M * ld);
+                max_b = std::max(max_b, rows * ld);
+                max_c = std::max(max_c, (size_t)M * rows);
             }
         }
     }
-    *out = default_config(M, K, N);
-    return SKG_OK;
+    int nd = 0;
+    {
+        std::vector<skg_config> uniq;
+        for (auto &t : todo) {
+            bool seen = false;
+            for (auto &u : uniq) seen = seen || config_equal(u, t.first);
+            if (!seen) uniq.push_back(t.first);
+        }
+        nd = (int)uniq.size();
+    }
+    if (n_configs_out) *n_configs_out = nd;
+    if (todo.empty()) return SKG_OK;
+    if (need_f > 0 || need_t > 0) {
+        Workspace w;
+        const int st = get_workspace(stream, need_f, need_t, &w);
+        if (st != SKG_OK) return st;
+    }
+    uint16_t *a = nullptr, *b = nullptr;
+    float *c = nullptr;
+    if (hipMalloc(&a, max_a * 2) != hipSuccess) return SKG_ERR_HIP;
+    const size_t b_bytes = max_b * (f32w ? 4 : 2);  // weights: bf16 or fp32
+    if (hipMalloc(&b, b_bytes) != hipSuccess) {
+        (void)hipFree(a);
+        return SKG_ERR_HIP;
+    }
+    if (hipMalloc(&c, max_c * 4) != hipSuccess) {
+        (void)hipFree(a);
+        (void)hipFree(b);
+        return SKG_ERR_HIP;
+    }
+    int rc = SKG_OK;
+    if (hipMemsetAsync(a, 0, max_a * 2, stream) != hipSuccess ||
+        hipMemsetAsync(b, 0, b_bytes, stream) != hipSuccess)
+        rc = SKG_ERR_HIP;
+    for (auto &t : todo) {
+        if (rc != SKG_OK) break;
+        const int M = t.second.first, K = t.second.second;
+        Geometry g;
+        make_geometry(M, K, 1, t.first, &g);
+        const int ld = round_up(K, kChunk);
+        rc = run(a, b, c, M, g.rows_per_wg, K, ld, ld, g.rows_per_wg, SKG_OUT_F32, stream,
+                 t.first, nullptr, nullptr, f32w);
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess && rc == SKG_OK) rc = SKG_ERR_HIP;
+    (void)hipFree(a);
+    (void)hipFree(b);
+    (void)hipFree(c);
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int skinny_gemm_dispatch(int M, int K, int N, skg_config *out) {
+    return dispatch_impl(M, K, N, false, out);
 }
 
 int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg) {
     if (!cfg) return SKG_ERR_INVALID_ARG;
-    Geometry g;
-    return make_geometry(M, K, N, *cfg, &g) ? SKG_OK : SKG_ERR_INVALID_ARG;
+    return config_ok(M, K, N, *cfg, false) ? SKG_OK : SKG_ERR_INVALID_ARG;
 }
 
 int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg, size_t *bytes) {
@@ -363,109 +495,61 @@ int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M, i
 
 int skinny_gemm_warmup_keys(const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
                             skg_config *out, int capacity, int *n_out) {
-    if (n_shapes < 0 || n_m < 0 || capacity < 0 || !n_out) return SKG_ERR_INVALID_ARG;
-    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values) || (capacity > 0 && !out))
-        return SKG_ERR_INVALID_ARG;
-    std::vector<skg_config> keys;
-    for (int i = 0; i < n_shapes; ++i) {
-        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
-        for (int j = 0; j < n_m; ++j) {
-            skg_config c;
-            const int st = skinny_gemm_dispatch(m_values[j], K, N, &c);
-            if (st != SKG_OK) return st;
-            bool seen = false;
-            for (const skg_config &k : keys) seen = seen || config_equal(k, c);
-            if (!seen) keys.push_back(c);
-        }
-    }
-    for (int i = 0; i < (int)keys.size() && i < capacity; ++i) out[i] = keys[i];
-    *n_out = (int)keys.size();
-    return SKG_OK;
+    return warmup_keys_impl(false, kn_pairs, n_shapes, m_values, n_m, out, capacity, n_out);
 }
 
 int skinny_gemm_warmup(const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
                        void *stream_v, int *n_configs_out) {
-    if (n_shapes < 0 || n_m < 0) return SKG_ERR_INVALID_ARG;
-    if ((n_shapes > 0 && !kn_pairs) || (n_m > 0 && !m_values)) return SKG_ERR_INVALID_ARG;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-    // the distinct configurations, the workspace they need, and a scratch
-    // problem large enough to run each of them once
-    std::vector<std::pair<skg_config, std::pair<int, int>>> todo;  // cfg, (M, K)
-    size_t need_f = 0, need_t = 0, max_a = 0, max_b = 0, max_c = 0;
-    for (int i = 0; i < n_shapes; ++i) {
-        const int K = kn_pairs[2 * i], N = kn_pairs[2 * i + 1];
-        if (K < 0 || N < 1) return SKG_ERR_INVALID_ARG;
-        for (int j = 0; j < n_m; ++j) {
-            const int M = m_values[j];
-            skg_config c;
-            const int st = skinny_gemm_dispatch(M, K, N, &c);
-            if (st != SKG_OK) return st;
-            if (K == 0) continue;
-            Geometry g;
-            if (!make_geometry(M, K, N, c, &g)) return SKG_ERR_INVALID_ARG;
-            need_f = std::max(need_f, g.ws_floats);
-            need_t = std::max(need_t, g.n_tickets);
-            bool seen = false;
-            for (auto &t : todo)
-                seen = seen || (config_equal(t.first, c) && t.second.first == M &&
-                                t.second.second == K);
-            if (!seen) {
-                todo.push_back({c, {M, K}});
-                const size_t rows = (size_t)g.rows_per_wg;
-                const size_t ld = (size_t)round_up(K, kChunk);
-                max_a = std::max(max_a, (size_t)M * ld);
-                max_b = std::max(max_b, rows * ld);
-                max_c = std::max(max_c, (size_t)M * rows);
-            }
-        }
-    }
-    int nd = 0;
-    {
-        std::vector<skg_config> uniq;
-        for (auto &t : todo) {
-            bool seen = false;
-            for (auto &u : uniq) seen = seen || config_equal(u, t.first);
-            if (!seen) uniq.push_back(t.first);
-        }
-        nd = (int)uniq.size();
-    }
-    if (n_configs_out) *n_configs_out = nd;
-    if (todo.empty()) return SKG_OK;
-    if (need_f > 0 || need_t > 0) {
-        Workspace w;
-        const int st = get_workspace(stream, need_f, need_t, &w);
-        if (st != SKG_OK) return st;
-    }
-    uint16_t *a = nullptr, *b = nullptr;
-    float *c = nullptr;
-    if (hipMalloc(&a, max_a * 2) != hipSuccess) return SKG_ERR_HIP;
-    if (hipMalloc(&b, max_b * 2) != hipSuccess) {
-        (void)hipFree(a);
-        return SKG_ERR_HIP;
-    }
-    if (hipMalloc(&c, max_c * 4) != hipSuccess) {
-        (void)hipFree(a);
-        (void)hipFree(b);
-        return SKG_ERR_HIP;
-    }
-    int rc = SKG_OK;
-    if (hipMemsetAsync(a, 0, max_a * 2, stream) != hipSuccess ||
-        hipMemsetAsync(b, 0, max_b * 2, stream) != hipSuccess)
-        rc = SKG_ERR_HIP;
-    for (auto &t : todo) {
-        if (rc != SKG_OK) break;
-        const int M = t.second.first, K = t.second.second;
-        Geometry g;
-        make_geometry(M, K, 1, t.first, &g);
-        const int ld = round_up(K, kChunk);
-        rc = run(a, b, c, M, g.rows_per_wg, K, ld, ld, g.rows_per_wg, SKG_OUT_F32, stream,
-                 t.first);
-    }
-    if (hipStreamSynchronize(stream) != hipSuccess && rc == SKG_OK) rc = SKG_ERR_HIP;
-    (void)hipFree(a);
-    (void)hipFree(b);
-    (void)hipFree(c);
-    return rc;
+    return warmup_impl(false, kn_pairs, n_shapes, m_values, n_m, stream_v, n_configs_out);
+}
+
+// ---- fp32 weights --------------------------------------------------------------
+
+int skinny_gemm_f32w_dispatch(int M, int K, int N, skg_config *out) {
+    return dispatch_impl(M, K, N, true, out);
+}
+
+int skinny_gemm_f32w_check_config(int M, int K, int N, const skg_config *cfg) {
+    if (!cfg) return SKG_ERR_INVALID_ARG;
+    return config_ok(M, K, N, *cfg, true) ? SKG_OK : SKG_ERR_INVALID_ARG;
+}
+
+int skinny_gemm_f32w_timed(const void *A, const void *W, void *C, int M, int N, int K,
+                           int64_t lda, int64_t ldw, int64_t ldc, int out_dtype, void *stream,
+                           void *start_event, void *stop_event) {
+    const int st = check_args(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, true);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    skg_config cfg;
+    const int ds = dispatch_impl(M, K, N, true, &cfg);
+    if (ds != SKG_OK) return ds;
+    return run(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, stream, cfg, start_event, stop_event,
+               true);
+}
+
+int skinny_gemm_f32w(const void *A, const void *W, void *C, int M, int N, int K, int64_t lda,
+                     int64_t ldw, int64_t ldc, int out_dtype, void *stream) {
+    return skinny_gemm_f32w_timed(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, stream, nullptr,
+                                  nullptr);
+}
+
+int skinny_gemm_f32w_with_config(const void *A, const void *W, void *C, int M, int N, int K,
+                                 int64_t lda, int64_t ldw, int64_t ldc, int out_dtype,
+                                 void *stream, const skg_config *cfg) {
+    if (!cfg) return SKG_ERR_INVALID_ARG;
+    const int st = check_args(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, true);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    if (K > 0 && !config_ok(M, K, N, *cfg, true)) return SKG_ERR_INVALID_ARG;
+    return run(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, stream, *cfg, nullptr, nullptr, true);
+}
+
+int skinny_gemm_f32w_warmup_keys(const int *kn_pairs, int n_shapes, const int *m_values,
+                                 int n_m, skg_config *out, int capacity, int *n_out) {
+    return warmup_keys_impl(true, kn_pairs, n_shapes, m_values, n_m, out, capacity, n_out);
+}
+
+int skinny_gemm_f32w_warmup(const int *kn_pairs, int n_shapes, const int *m_values, int n_m,
+                            void *stream_v, int *n_configs_out) {
+    return warmup_impl(true, kn_pairs, n_shapes, m_values, n_m, stream_v, n_configs_out);
 }
 
 int skinny_gemm_stream_read(const void *src, size_t bytes, void *sink, void *stream) {

@@ -134,6 +134,27 @@ __device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b, float c) {
     return c;
 }
 
+// Eight bf16 activations times eight fp32 weights (w0: elements 0..3, w1:
+// 4..7), one fused multiply-add each, in element order.  The bf16 -> fp32
+// widening is exact (the 16 bits become the upper half of the fp32 word).
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) {
+    return __builtin_bit_cast(float, x & 0xFFFF0000u);
+}
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ float dot8_f32w(const uint4 &a, const uint4 &w0, const uint4 &w1,
+                                           float c) {
+    c = __builtin_fmaf(bf_lo(a.x), u2f(w0.x), c);
+    c = __builtin_fmaf(bf_hi(a.x), u2f(w0.y), c);
+    c = __builtin_fmaf(bf_lo(a.y), u2f(w0.z), c);
+    c = __builtin_fmaf(bf_hi(a.y), u2f(w0.w), c);
+    c = __builtin_fmaf(bf_lo(a.z), u2f(w1.x), c);
+    c = __builtin_fmaf(bf_hi(a.z), u2f(w1.y), c);
+    c = __builtin_fmaf(bf_lo(a.w), u2f(w1.z), c);
+    c = __builtin_fmaf(bf_hi(a.w), u2f(w1.w), c);
+    return c;
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -162,12 +183,27 @@ __device__ __forceinline__ int64_t window_off(int c, const KParams &p) {
     return (int64_t)min(c * kChunk, p.K - kChunk);
 }
 
+// First window position that belongs to chunk c (0 inside K, 8 beyond it).
+__device__ __forceinline__ int tail_j0(int c, const KParams &p) {
+    return (c < p.nfull) ? 0 : (c < p.nck ? kChunk - (p.K - p.nfull * kChunk) : kChunk);
+}
+
 __device__ __forceinline__ uint4 tail_mask(int c, const KParams &p) {
-    const int j0 = (c < p.nfull) ? 0 : (c < p.nck ? kChunk - (p.K - p.nfull * kChunk) : kChunk);
+    const int j0 = tail_j0(c, p);
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         w[d] = ((2 * d >= j0) ? 0x0000FFFFu : 0u) | ((2 * d + 1 >= j0) ? 0xFFFF0000u : 0u);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The same mask for half h (window positions 4h .. 4h + 3) of a window of
+// eight fp32 weights.
+__device__ __forceinline__ uint4 tail_mask_f32(int c, const KParams &p, int h) {
+    const int j0 = tail_j0(c, p);
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] = (4 * h + d >= j0) ? 0xFFFFFFFFu : 0u;
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -434,8 +470,11 @@ __device__ __forceinline__ void staged_barrier() {
 // PF: K-steps of B loads in flight (register ring depth); AG: each step's
 // activation chunks are loaded from global memory (L2-resident) into the same
 // ring as B, instead of being staged in LDS before the stream (no staging
-// latency and no barrier; M more loads per step).
-template <int M, int R, int PF, bool AG>
+// latency and no barrier; M more loads per step).  WF: the weights are fp32
+// (p.B points to fp32 rows of p.ldb elements): a lane's chunk of eight k is
+// then 32 bytes of a row, read as two 16-byte loads from the same window,
+// and each product is one fp32 fused multiply-add of the widened activation.
+template <int M, int R, int PF, bool AG, bool WF = false>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
@@ -458,22 +497,28 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     const int rl0 = wn * (4 * R) + slot;  // local row of slot r = 0
 
     // load cursor: row block lb, step lst; once past the last row block the
-    // loads read row 0 of A instead (in bounds, cache-resident, never used)
+    // loads read row 0 of A instead (in bounds, cache-resident, never used;
+    // with fp32 weights row 0 of B, which holds the 2K bytes such a load
+    // may reach)
+    constexpr int WL = WF ? 2 : 1;  // 16-byte loads per row and step
     int lb = 0, lst = 0;
-    const uint16_t *rowp[R];
+    const uint16_t *rowp[R];  // row starts, in 16-bit units
     auto set_rows = [&](int b) {
         int bst = 0, bcnt = 1;
         if (b < w.nblk) block_rows(p, w.rb0 + b * w.rbs, bst, bcnt);
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            rowp[r] = (b < w.nblk) ? p.B + (int64_t)(bst + min(rl0 + 4 * r, bcnt - 1)) * p.ldb
-                                   : p.A;
+            rowp[r] = (b < w.nblk)
+                          ? p.B + (int64_t)(bst + min(rl0 + 4 * r, bcnt - 1)) * p.ldb * WL
+                          : (WF ? p.B : p.A);
     };
     constexpr int NA = AG ? M : 1;
-    auto issue = [&](uint4(&dst)[R], uint4(&adst)[NA]) {
+    auto issue = [&](uint4(&dst)[R][WL], uint4(&adst)[NA]) {
         const int64_t off = window_off(wv_c0 + lst * kValuStep + l16, p);
 #pragma unroll
-        for (int r = 0; r < R; ++r) dst[r] = ldg16_stream(rowp[r] + off);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int h = 0; h < WL; ++h) dst[r][h] = ldg16_stream(rowp[r] + WL * off + 8 * h);
         if constexpr (AG)
 #pragma unroll
             for (int m = 0; m < M; ++m) adst[m] = ldg16(p.A + (int64_t)m * p.lda + off);
@@ -483,7 +528,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         }
     };
 
-    uint4 buf[PF][R];
+    uint4 buf[PF][R][WL];
     uint4 abuf[PF][NA];
     set_rows(0);
     if constexpr (AG) {
@@ -495,7 +540,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         stage_a(p, As, w.wg_c0);
 #pragma unroll
         for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
-        staged_barrier<PF * R>();
+        staged_barrier<PF * R * WL>();
     }
 
     float acc[R][M];
@@ -512,11 +557,21 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     const bool direct = direct_write(p);
 
     int cb = 0, cst = 0;  // compute cursor
-    auto step = [&](uint4(&bv)[R], uint4(&av)[NA]) {
+    auto step = [&](uint4(&bv)[R][WL], uint4(&av)[NA]) {
         if (cst >= tail_st) {
-            const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + l16, p);
+            const int c = wv_c0 + cst * kValuStep + l16;
+            const uint4 mk = tail_mask(c, p);
+            if constexpr (WF) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) bv[r] = and4(bv[r], mk);
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 mw = tail_mask_f32(c, p, h);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) bv[r][h] = and4(bv[r][h], mw);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) bv[r][0] = and4(bv[r][0], mk);
+            }
             if constexpr (AG)
 #pragma unroll
                 for (int m = 0; m < M; ++m) av[m] = and4(av[m], mk);
@@ -533,7 +588,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = dot8(a[m], bv[r], acc[r][m]);
+            for (int m = 0; m < M; ++m) {
+                if constexpr (WF)
+                    acc[r][m] = dot8_f32w(a[m], bv[r][0], bv[r][1], acc[r][m]);
+                else
+                    acc[r][m] = dot8(a[m], bv[r][0], acc[r][m]);
+            }
         if (++cst == SPB) {
             // row block done: lane m of each row group now takes token m
             const int rb = w.rb0 + cb * w.rbs;
@@ -1006,12 +1066,36 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
             [&](int m) { return 64 * (m >> 2) + (m & 3); });
 }
 
-// Instantiation list for one M, in the order of kValuVariants.
+// Over fp32 weights the register ring is twice as large, and these
+// (M, rows, depth) combinations would spill to scratch (measured with the
+// compiler's resource-usage report), so they are not built: the largest M
+// per (R, PF), with activations staged in LDS (AG false) or in the ring.
+constexpr int f32w_max_m(int R, int PF, bool AG) {
+    return !AG ? ((R == 4 && PF == 4) ? 8 : (R == 2 && PF == 8) ? 10 : (R == 4 && PF == 2) ? 12 : 16)
+               : ((PF == 12 || (R == 2 && PF == 8)) ? 2 : (R == 4 && PF == 4) ? 4
+                  : (R == 1 && PF == 8) ? 5 : (R == 2 && PF == 4) ? 7 : 8);
+}
+
+template <int M, int R, int PF, bool AG>
+constexpr KernelPtr f32w_kernel() {
+    if constexpr (M <= f32w_max_m(R, PF, AG))
+        return skg_valu_kernel<M, R, PF, AG, true>;
+    else
+        return nullptr;
+}
+
+// Instantiation list for one M, in the order of kValuVariants (bf16
+// weights; SKG_VALU_ROW_F32W: fp32 weights, nullptr where not built).
 #define SKG_VALU_ROW(M, AG)                                                              \
     {skg_valu_kernel<M, 1, 4, AG>, skg_valu_kernel<M, 1, 8, AG>,                         \
      skg_valu_kernel<M, 1, 12, AG>, skg_valu_kernel<M, 2, 2, AG>,                        \
      skg_valu_kernel<M, 2, 4, AG>, skg_valu_kernel<M, 2, 8, AG>,                         \
      skg_valu_kernel<M, 4, 2, AG>, skg_valu_kernel<M, 4, 4, AG>}
+#define SKG_VALU_ROW_F32W(M, AG)                                                         \
+    {f32w_kernel<M, 1, 4, AG>(), f32w_kernel<M, 1, 8, AG>(),                             \
+     f32w_kernel<M, 1, 12, AG>(), f32w_kernel<M, 2, 2, AG>(),                            \
+     f32w_kernel<M, 2, 4, AG>(), f32w_kernel<M, 2, 8, AG>(),                             \
+     f32w_kernel<M, 4, 2, AG>(), f32w_kernel<M, 4, 4, AG>()}
 
 }  // namespace
 }  // namespace skg

@@ -47,6 +47,7 @@ struct KParams {
                       // that the epilogue combines
     int flag_offset;  // byte offset of the split-K "last arrival" flag in LDS
     int tr_offset;    // byte offset of the MFMA kernel's per-wave transpose tiles
+    int w_f32;        // B holds fp32 weights (rows of ldb fp32 elements)
 };
 
 // Derived launch geometry for (M, K, N, cfg).
@@ -67,10 +68,13 @@ struct Geometry {
 // Fills g; returns false if cfg cannot run (M, K, N).
 bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g);
 
-// Whether (inner, row_tiles, depth) has a compiled kernel.
-bool variant_exists(int inner, int row_tiles, int depth);
+// Whether (inner, row_tiles, depth) has a compiled kernel (f32w: one over fp32
+// weights for M tokens; those exist for the VALU kinds only, and not for
+// every M).
+bool variant_exists(int inner, int row_tiles, int depth, bool f32w = false, int M = 1);
 
-// Enqueues the kernel for p with geometry g on stream.  Non-null start/stop
+// Enqueues the kernel for p (p.w_f32 selects the fp32-weight kernels) with
+// geometry g on stream.  Non-null start/stop
 // events are recorded by the dispatch itself (kernel start and end).
 hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
                   hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
@@ -81,7 +85,7 @@ hipError_t launch_zero_fill(void *C, int M, int N, int64_t ldc, int out_bf16,
                             hipEvent_t stop = nullptr);
 
 // K in 1..7: one thread per output, plain fp32 sum (p needs A, B, C, lda,
-// ldb, ldc, M, N, K, out_bf16).
+// ldb, ldc, M, N, K, out_bf16, w_f32).
 hipError_t launch_small_k(const KParams &p, hipStream_t stream, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
 
@@ -106,5 +110,9 @@ constexpr int kNumValu = sizeof(kValuVariants) / sizeof(kValuVariants[0]);
 KernelPtr valu_kernel_lo(int M, int variant);
 KernelPtr valu_kernel_hi(int M, int variant);
 KernelPtr valu_kernel_ga(int M, int variant);  // activations from global memory, M <= 8
+// the same three tables over fp32 weights (skg_f32w_lo/hi/ga.hip)
+KernelPtr valu_kernel_f32w_lo(int M, int variant);
+KernelPtr valu_kernel_f32w_hi(int M, int variant);
+KernelPtr valu_kernel_f32w_ga(int M, int variant);
 
 }  // namespace skg

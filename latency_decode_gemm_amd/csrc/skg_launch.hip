@@ -24,7 +24,8 @@ __global__ void skg_zero_fill_kernel(void *C, int M, int N, int64_t ldc, int out
 }
 
 // K < 8: every row is shorter than one 16-byte window, so each output is a
-// plain fp32 sum over k of elementwise products (one thread per output).
+// plain fp32 sum over k of elementwise products (one thread per output; the
+// weights are bf16 or, with p.w_f32, fp32).
 __global__ void skg_small_k_kernel(KParams p) {
     const int64_t total = (int64_t)p.M * p.N;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -32,11 +33,17 @@ __global__ void skg_small_k_kernel(KParams p) {
         const int m = (int)(i / p.N);
         const int n = (int)(i - (int64_t)m * p.N);
         const uint16_t *a = p.A + (int64_t)m * p.lda;
-        const uint16_t *b = p.B + (int64_t)n * p.ldb;
         float v = 0.0f;
-        for (int k = 0; k < p.K; ++k)
-            v = fmaf(__builtin_bit_cast(float, (uint32_t)a[k] << 16),
-                     __builtin_bit_cast(float, (uint32_t)b[k] << 16), v);
+        if (p.w_f32) {
+            const float *b = reinterpret_cast<const float *>(p.B) + (int64_t)n * p.ldb;
+            for (int k = 0; k < p.K; ++k)
+                v = fmaf(__builtin_bit_cast(float, (uint32_t)a[k] << 16), b[k], v);
+        } else {
+            const uint16_t *b = p.B + (int64_t)n * p.ldb;
+            for (int k = 0; k < p.K; ++k)
+                v = fmaf(__builtin_bit_cast(float, (uint32_t)a[k] << 16),
+                         __builtin_bit_cast(float, (uint32_t)b[k] << 16), v);
+        }
         store_c(p, m, n, v);
     }
 }
@@ -116,15 +123,21 @@ const MfmaVariant kMfmaVariants[] = {SKG_MFMA(1, 2), SKG_MFMA(1, 3), SKG_MFMA(1,
 #undef SKG_MFMA
 constexpr int kNumMfma = sizeof(kMfmaVariants) / sizeof(kMfmaVariants[0]);
 
-KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
+KernelPtr find_kernel(int inner, int M, int row_tiles, int depth, bool f32w) {
     if (inner == SKG_INNER_VALU || inner == SKG_INNER_VALU_GA) {
         for (int i = 0; i < kNumValu; ++i)
             if (kValuVariants[i][0] == row_tiles && kValuVariants[i][1] == depth) {
+                if (f32w) {
+                    if (inner == SKG_INNER_VALU_GA)
+                        return M <= 8 ? valu_kernel_f32w_ga(M, i) : nullptr;
+                    return M <= 8 ? valu_kernel_f32w_lo(M, i) : valu_kernel_f32w_hi(M, i);
+                }
                 if (inner == SKG_INNER_VALU_GA) return M <= 8 ? valu_kernel_ga(M, i) : nullptr;
                 return M <= 8 ? valu_kernel_lo(M, i) : valu_kernel_hi(M, i);
             }
         return nullptr;
     }
+    if (f32w) return nullptr;  // matrix-core kernels take bf16 weights only
     for (int i = 0; i < kNumMfma; ++i) {
         const MfmaVariant &v = kMfmaVariants[i];
         if (v.G != row_tiles || v.PF != depth) continue;
@@ -141,13 +154,13 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth) {
 
 }  // namespace
 
-bool variant_exists(int inner, int row_tiles, int depth) {
-    return find_kernel(inner, 1, row_tiles, depth) != nullptr;
+bool variant_exists(int inner, int row_tiles, int depth, bool f32w, int M) {
+    return find_kernel(inner, M, row_tiles, depth, f32w) != nullptr;
 }
 
 hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
                   hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth);
+    KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth, p.w_f32 != 0);
     if (!fn) return hipErrorInvalidValue;
     if (g.lds_bytes > 64 * 1024) {
         // allow this kernel the full LDS of a CU (once per kernel)

@@ -3,7 +3,8 @@
 Tensors are PyTorch device tensors; every computation runs in the HIP
 library.  dtype guards live here because the C ABI takes ``void*``: both
 operands must be bf16 (the router gate on the PR #42562 page, section
-评论区精华, requires bf16 for the activations and for the weight).
+评论区精华, requires bf16 for the activations and for the weight), except
+for the ``skinny_gemm_f32w*`` entry points, whose weights are fp32.
 """
 from __future__ import annotations
 
@@ -32,9 +33,13 @@ def _round8(x: int) -> int:
     return (x + 7) // 8 * 8
 
 
-def _marshal(A, B, out, out_dtype):
+def _marshal(A, B, out, out_dtype, f32w=False):
     torch = _torch()
-    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+    if f32w:
+        if A.dtype != torch.bfloat16 or B.dtype != torch.float32:
+            raise TypeError(f"A must be torch.bfloat16 and W torch.float32 (got {A.dtype}, "
+                            f"{B.dtype})")
+    elif A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError(f"A and B must be torch.bfloat16 (got {A.dtype}, {B.dtype})")
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A must be [M, K] and B [N, K]")
@@ -63,7 +68,7 @@ def _marshal(A, B, out, out_dtype):
         raise ValueError("A, B and out must be on the same device")
     # a stride is only meaningful when there is a second row
     lda = A.stride(0) if M > 1 else max(_round8(K), 8)
-    ldb = B.stride(0) if N > 1 else max(_round8(K), 8)
+    ldb = B.stride(0) if N > 1 else max(_round8(K), 8)  # elements of B's dtype
     ldc = out.stride(0) if M > 1 else max(N, 1)
     return M, N, K, lda, ldb, ldc, odt, out
 
@@ -119,6 +124,51 @@ def skinny_gemm_workspace_bytes(M: int, K: int, N: int, cfg: SkgConfig) -> int:
     return int(n.value)
 
 
+def skinny_gemm_f32w(A, W, out=None, out_dtype=None, stream=None):
+    """C = A . W^T with A [M, K] bf16 and fp32 weights W [N, K] (the router
+    GEMM over fp32 weights; M <= 16) into ``out`` (fp32 or bf16).  Returns
+    ``out``."""
+    M, N, K, lda, ldw, ldc, odt, out = _marshal(A, W, out, out_dtype, f32w=True)
+    st = _capi.lib().skinny_gemm_f32w(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K,
+                                      lda, ldw, ldc, odt, _stream_handle(stream, A.device))
+    check(st, "skinny_gemm_f32w")
+    return out
+
+
+def skinny_gemm_f32w_timed(A, W, start_event, stop_event, out=None, out_dtype=None,
+                           stream=None):
+    """As :func:`skinny_gemm_f32w`, recording the kernel's own start and end."""
+    M, N, K, lda, ldw, ldc, odt, out = _marshal(A, W, out, out_dtype, f32w=True)
+    h0 = getattr(start_event, "handle", start_event)
+    h1 = getattr(stop_event, "handle", stop_event)
+    st = _capi.lib().skinny_gemm_f32w_timed(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K,
+                                            lda, ldw, ldc, odt, _stream_handle(stream, A.device),
+                                            h0, h1)
+    check(st, "skinny_gemm_f32w_timed")
+    return out
+
+
+def skinny_gemm_f32w_with_config(A, W, cfg: SkgConfig, out=None, out_dtype=None, stream=None):
+    """As :func:`skinny_gemm_f32w` with an explicit kernel configuration."""
+    M, N, K, lda, ldw, ldc, odt, out = _marshal(A, W, out, out_dtype, f32w=True)
+    st = _capi.lib().skinny_gemm_f32w_with_config(
+        A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, lda, ldw, ldc, odt,
+        _stream_handle(stream, A.device), ctypes.byref(cfg))
+    check(st, "skinny_gemm_f32w_with_config")
+    return out
+
+
+def skinny_gemm_f32w_dispatch(M: int, K: int, N: int) -> SkgConfig:
+    cfg = SkgConfig()
+    check(_capi.lib().skinny_gemm_f32w_dispatch(M, K, N, ctypes.byref(cfg)),
+          "skinny_gemm_f32w_dispatch")
+    return cfg
+
+
+def skinny_gemm_f32w_check_config(M: int, K: int, N: int, cfg: SkgConfig) -> bool:
+    return _capi.lib().skinny_gemm_f32w_check_config(M, K, N, ctypes.byref(cfg)) == _capi.SKG_OK
+
+
 def _pairs(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
     flat = [v for kn in shapes for v in (int(kn[0]), int(kn[1]))]
     ms = [int(m) for m in m_values]
@@ -127,32 +177,50 @@ def _pairs(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
     return kn_arr, len(flat) // 2, m_arr, len(ms)
 
 
+def _warmup_keys(fn_name, shapes, m_values):
+    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
+    fn = getattr(_capi.lib(), fn_name)
+    n = ctypes.c_int(0)
+    check(fn(kn_arr, ns, m_arr, nm, None, 0, ctypes.byref(n)), fn_name)
+    buf = (SkgConfig * max(n.value, 1))()
+    check(fn(kn_arr, ns, m_arr, nm, buf, n.value, ctypes.byref(n)), fn_name)
+    return [SkgConfig(*buf[i].as_tuple()) for i in range(n.value)]
+
+
+def _warmup(fn_name, shapes, m_values, stream, device):
+    torch = _torch()
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
+    n = ctypes.c_int(0)
+    with torch.cuda.device(device):
+        check(getattr(_capi.lib(), fn_name)(kn_arr, ns, m_arr, nm,
+                                            _stream_handle(stream, device), ctypes.byref(n)),
+              fn_name)
+    return int(n.value)
+
+
 def skinny_gemm_warmup_keys(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
     """Distinct dispatch results over (K, N) in ``shapes`` x M in
     ``m_values``, first-seen order."""
-    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
-    n = ctypes.c_int(0)
-    check(_capi.lib().skinny_gemm_warmup_keys(kn_arr, ns, m_arr, nm, None, 0, ctypes.byref(n)),
-          "skinny_gemm_warmup_keys")
-    buf = (SkgConfig * max(n.value, 1))()
-    check(_capi.lib().skinny_gemm_warmup_keys(kn_arr, ns, m_arr, nm, buf, n.value,
-                                              ctypes.byref(n)), "skinny_gemm_warmup_keys")
-    return [SkgConfig(*buf[i].as_tuple()) for i in range(n.value)]
+    return _warmup_keys("skinny_gemm_warmup_keys", shapes, m_values)
 
 
 def skinny_gemm_warmup(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int],
                        stream=None, device=None) -> int:
     """Loads code, sizes the stream's split-K workspace and runs each distinct
     configuration once.  Returns the number of distinct configurations."""
-    torch = _torch()
-    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-    kn_arr, ns, m_arr, nm = _pairs(shapes, m_values)
-    n = ctypes.c_int(0)
-    with torch.cuda.device(device):
-        check(_capi.lib().skinny_gemm_warmup(kn_arr, ns, m_arr, nm,
-                                             _stream_handle(stream, device), ctypes.byref(n)),
-              "skinny_gemm_warmup")
-    return int(n.value)
+    return _warmup("skinny_gemm_warmup", shapes, m_values, stream, device)
+
+
+def skinny_gemm_f32w_warmup_keys(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int]):
+    """As :func:`skinny_gemm_warmup_keys` for fp32 weights."""
+    return _warmup_keys("skinny_gemm_f32w_warmup_keys", shapes, m_values)
+
+
+def skinny_gemm_f32w_warmup(shapes: Sequence[Tuple[int, int]], m_values: Iterable[int],
+                            stream=None, device=None) -> int:
+    """As :func:`skinny_gemm_warmup` for fp32 weights."""
+    return _warmup("skinny_gemm_f32w_warmup", shapes, m_values, stream, device)
 
 
 def skinny_gemm_stream_read(src, sink, nbytes: Optional[int] = None, stream=None):

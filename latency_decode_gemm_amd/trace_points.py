@@ -11,7 +11,8 @@ call (the zero-fill kernel, a marker), ``trace_warm`` warm-up calls and
 for the two-pass split-K backend).  The library's dispatches are taken in
 time order; the ones after the i-th marker belong to the i-th point.  A
 call's kernel time is the sum of its dispatches' durations; the table gives
-the median over the timed calls, the weight bandwidth 2NK / time and the
+the median over the timed calls, the weight bandwidth (weight bytes: 2NK,
+or 4NK over fp32 weights) / time and the
 fraction of 8 TB/s, beside the bench's own figures for the point, taken from
 ``plain.json`` when given: the output of the same command run without the
 profiler, whose event, eager and graph timings the tracing does not inflate.

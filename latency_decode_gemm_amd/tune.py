@@ -24,6 +24,7 @@ import time
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
+TABLE_F32W = os.path.join(PKG, "csrc", "tuned_table_f32w.inc")
 
 from latency_decode_gemm_amd._capi import MFMA_VARIANTS, VALU_VARIANTS
 WAVES = [(1, 1), (2, 1), (3, 1), (4, 1), (6, 1), (8, 1), (1, 2), (2, 2), (3, 2), (4, 2),
@@ -36,8 +37,9 @@ def rows_per_wave(inner, rt):
     return 4 * rt if inner in (0, 3) else 16 * rt  # inner 1, 2: MFMA tiles of 16 rows
 
 
-def structures(skg, M, K, N, inner_set):
+def structures(skg, M, K, N, inner_set, check=None):
     """(inner, rt, depth, wn, wk, S, rb_per_wg) tuples for stage 1."""
+    check = check or skg.skinny_gemm_check_config
     out = []
     # two ring depths per structure (a shallow ring often wins when a
     # workgroup streams few steps)
@@ -65,7 +67,7 @@ def structures(skg, M, K, N, inner_set):
                             cfg = skg.SkgConfig.make(backend=be, inner=inner, split_k=S,
                                                      row_tiles=rt, waves_n=wn, waves_k=wk,
                                                      depth=d, rb_per_wg=rpw)
-                            if skg.skinny_gemm_check_config(M, K, N, cfg):
+                            if check(M, K, N, cfg):
                                 out.append(cfg)
                 # rows dealt evenly to 256 or 512 workgroups (backend 3), as
                 # row blocks x K slices, when the waves cover a block with
@@ -78,13 +80,14 @@ def structures(skg, M, K, N, inner_set):
                         cfg = skg.SkgConfig.make(backend=3, inner=inner, split_k=S,
                                                  row_tiles=rt, waves_n=wn, waves_k=wk, depth=d,
                                                  rb_per_wg=per_cu)
-                        if skg.skinny_gemm_check_config(M, K, N, cfg):
+                        if check(M, K, N, cfg):
                             out.append(cfg)
     return out
 
 
-def variants_of(skg, M, K, N, cfg):
+def variants_of(skg, M, K, N, cfg, check=None):
     """Stage-2 neighbours: other depths/row tiles of the same family and grid sizes."""
+    check = check or skg.skinny_gemm_check_config
     out = []
     fam = VALU_VARIANTS if cfg.inner in (0, 3) else MFMA_VARIANTS
     for (rt, d) in fam:
@@ -94,7 +97,7 @@ def variants_of(skg, M, K, N, cfg):
             c = skg.SkgConfig.make(backend=cfg.backend, inner=cfg.inner, split_k=cfg.split_k,
                                    row_tiles=rt, waves_n=cfg.waves_n, waves_k=cfg.waves_k,
                                    depth=d, rb_per_wg=rpw)
-            if skg.skinny_gemm_check_config(M, K, N, c):
+            if check(M, K, N, c):
                 out.append(c)
     return out
 
@@ -122,14 +125,20 @@ def choose(timed, parity_ok):
 
 
 class Bench:
-    """Rotating weight copies and a timing helper for one (K, N)."""
+    """Rotating weight copies and a timing helper for one (K, N); f32w: fp32
+    weights (``bits`` then holds the float32 array)."""
 
-    def __init__(self, torch, inputs, K, N, rotate_bytes=1 << 30):
+    def __init__(self, torch, inputs, K, N, rotate_bytes=1 << 30, f32w=False):
         self.torch = torch
         self.K, self.N = K, N
-        self.bits = inputs.make_b(K, N)
-        base = torch.from_numpy(self.bits.view("int16")).cuda().view(torch.bfloat16)
-        n = max(2, math.ceil(rotate_bytes / (2 * N * K)))
+        self.f32w = f32w
+        if f32w:
+            self.bits = inputs.make_w_f32(K, N)
+            base = torch.from_numpy(self.bits).cuda()
+        else:
+            self.bits = inputs.make_b(K, N)
+            base = torch.from_numpy(self.bits.view("int16")).cuda().view(torch.bfloat16)
+        n = max(2, math.ceil(rotate_bytes / (base.element_size() * N * K)))
         self.copies = [base] + [base.clone() for _ in range(n - 1)]
         self.nxt = 0
 
@@ -144,10 +153,12 @@ def time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg, stream, calls, r
     h = stream.cuda_stream
     K, N = bench.K, bench.N
 
+    fn = lib.skinny_gemm_f32w_with_config if bench.f32w else lib.skinny_gemm_bf16_with_config
+
     def one():
         B = bench.next()
-        st = lib.skinny_gemm_bf16_with_config(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
-                                              K, K, ldc, odt, h, ctypes.byref(cfg))
+        st = fn(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, K, K, ldc, odt, h,
+                ctypes.byref(cfg))
         if st != 0:
             raise RuntimeError(f"status {st} for {cfg}")
 
@@ -172,14 +183,19 @@ def time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg, stream, calls, r
 
 
 def sampled_parity(oracle, acceptance, np, A_bits, B_bits, C, M, K, N, out):
+    """Sampled columns against the oracle (B_bits float32: fp32 weights)."""
     Cf = C[:, :N].float().cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(1)
     ns = np.sort(rng.choice(N, size=min(96, N), replace=False))
     ms = np.repeat(np.arange(M), ns.size)
     nn = np.tile(ns, M)
-    ref = oracle.gemm_points(A_bits, B_bits, K, ms, nn).reshape(M, ns.size)
     an = acceptance.row_norms(oracle.bf16_decode(A_bits), K)
-    bn = acceptance.row_norms(oracle.bf16_decode(B_bits[ns]), K)
+    if B_bits.dtype == np.float32:
+        ref = oracle.gemm_f32w_points(A_bits, B_bits, K, ms, nn).reshape(M, ns.size)
+        bn = acceptance.row_norms(B_bits[ns].astype(np.float64), K)
+    else:
+        ref = oracle.gemm_points(A_bits, B_bits, K, ms, nn).reshape(M, ns.size)
+        bn = acceptance.row_norms(oracle.bf16_decode(B_bits[ns]), K)
     return acceptance.assess(Cf[:, ns], ref, an, bn, out)
 
 
@@ -201,15 +217,17 @@ def read_table(path=TABLE):
     return out
 
 
-def write_table(results, path=TABLE):
+def write_table(results, path=TABLE, f32w=False):
     lines = [
-        "// Tuned (M, K, N) -> configuration table, measured on MI355X (gfx950) by",
-        "// `python -m latency_decode_gemm_amd.tune --write`: each entry is the fastest",
+        "// Tuned (M, K, N) -> configuration table%s, measured on MI355X (gfx950) by"
+        % (" for fp32 weights" if f32w else ""),
+        "// `python -m latency_decode_gemm_amd.tune%s --write`: each entry is the fastest"
+        % (" --weights f32" if f32w else ""),
         "// configuration found for that shape (HIP-graph timing over weight copies",
         "// rotated past the Infinity Cache), checked against the CPU oracle.",
         "// Fields: M, K, N, {backend, inner, split_k, row_tiles, waves_n, waves_k,",
         "//                   depth, rb_per_wg}   // measured us per call",
-        "static const TableEntry kTunedTable[] = {",
+        "static const TableEntry %s[] = {" % ("kTunedTableF32w" if f32w else "kTunedTable"),
     ]
     for r in sorted(results, key=lambda r: (r["K"], r["N"], r["M"])):
         c = r["config"]
@@ -231,7 +249,11 @@ def main():
     ap.add_argument("--json", default=None, help="write all results/timings here")
     ap.add_argument("--calls", type=int, default=16)
     ap.add_argument("--top", type=int, default=6)
+    ap.add_argument("--weights", choices=("bf16", "f32"), default="bf16",
+                    help="f32: tune the fp32-weight entry points over their workload")
     args = ap.parse_args()
+    f32w = args.weights == "f32"
+    table_path = TABLE_F32W if f32w else TABLE
 
     import numpy as np
     import torch
@@ -243,17 +265,21 @@ def main():
     from latency_decode_gemm_amd import _capi, inputs
 
     lib = _capi.lib()
+    universe = inputs.WORKLOADS_F32W["router_f32w"] if f32w else inputs.all_points()
+    check = skg.skinny_gemm_f32w_check_config if f32w else skg.skinny_gemm_check_config
+    dispatch = skg.skinny_gemm_f32w_dispatch if f32w else skg.skinny_gemm_dispatch
+    run_cfg = skg.skinny_gemm_f32w_with_config if f32w else skg.skinny_gemm_bf16_with_config
     if args.points == "all":
-        pts = inputs.all_points()
+        pts = universe
     elif args.points in inputs.WORKLOADS:
         pts = inputs.WORKLOADS[args.points]
     else:
         want = [tuple(int(x) for x in s.split(",")) for s in args.points.split(";")]
-        pts = [p for p in inputs.all_points() if (p["M"], p["K"], p["N"]) in want]
+        pts = [p for p in universe if (p["M"], p["K"], p["N"]) in want]
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     # points not timed in this run keep their current entries
-    results = read_table()
+    results = read_table(table_path)
     if args.merge and os.path.exists(args.merge):
         with open(args.merge) as f:
             results = [r for r in json.load(f)["results"]]
@@ -262,7 +288,7 @@ def main():
     for p in pts:
         by_shape.setdefault((p["K"], p["N"]), []).append(p)
     for (K, N), group in by_shape.items():
-        bench = Bench(torch, inputs, K, N)
+        bench = Bench(torch, inputs, K, N, f32w=f32w)
         for p in group:
             t0 = time.time()
             M, out = p["M"], p["out"]
@@ -272,9 +298,9 @@ def main():
             odt = skg.SKG_OUT_BF16 if out == "bf16" else skg.SKG_OUT_F32
             C = torch.zeros((M, ldc), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                             device="cuda")
-            inner_set = ([0, 3] if M < 2 else [0, 3, 1, 2, 4, 5] if M <= 8 else
+            inner_set = ([0, 3] if M < 2 or f32w else [0, 3, 1, 2, 4, 5] if M <= 8 else
                          [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0])
-            cands = structures(skg, M, K, N, inner_set)
+            cands = structures(skg, M, K, N, inner_set, check)
             timed = {}
             print(f"M={M} K={K} N={N}: {len(cands)} stage-1 candidates", file=sys.stderr,
                   flush=True)
@@ -287,14 +313,14 @@ def main():
             best = sorted(timed, key=timed.get)[:args.top]
             stage2 = set()
             for b in best:
-                stage2.update(variants_of(skg, M, K, N, b))
+                stage2.update(variants_of(skg, M, K, N, b, check))
             for cfg in stage2:
                 if cfg not in timed:
                     timed[cfg] = time_config(torch, lib, skg, bench, A, C, M, ldc, odt, cfg,
                                              stream, args.calls, reps=1)
             final = sorted(timed, key=timed.get)[:args.top]
             # the current table entry competes in the final round too
-            default = skg.skinny_gemm_dispatch(M, K, N)
+            default = dispatch(M, K, N)
             if default not in final:
                 final.append(default)
             # and the best single dispatches, timed again with more repeats
@@ -307,7 +333,7 @@ def main():
 
             def parity_ok(cfg):
                 C.fill_(float("nan"))
-                skg.skinny_gemm_bf16_with_config(A, bench.copies[0], cfg, out=C[:, :N])
+                run_cfg(A, bench.copies[0], cfg, out=C[:, :N])
                 torch.cuda.synchronize()
                 r = sampled_parity(oracle, acceptance, np, A_bits, bench.bits, C, M, K, N, out)
                 if not r["ok"]:
@@ -336,8 +362,8 @@ def main():
         with open(args.json, "w") as f:
             json.dump({"results": results, "log": log}, f, indent=1)
     if args.write:
-        write_table(results)
-        print(f"wrote {TABLE} ({len(results)} entries)")
+        write_table(results, table_path, f32w)
+        print(f"wrote {table_path} ({len(results)} entries)")
 
 
 if __name__ == "__main__":

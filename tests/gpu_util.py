@@ -66,3 +66,24 @@ def cached_b(K: int, N: int, ldb: int | None = None) -> np.ndarray:
 
 def round8(x: int) -> int:
     return (x + 7) // 8 * 8
+
+
+def operands_f32w(A_bits: np.ndarray, W: np.ndarray, K: int):
+    """Device views A[:, :K] (bf16) and W[:, :K] (fp32) that keep the padded
+    leading dimensions."""
+    torch = torch_cuda()
+    A = to_dev(A_bits)
+    Wd = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to("cuda")
+    return A[:, :K], Wd[:, :K]
+
+
+def assess_f32w(C, A_bits, W, K, C_ref=None) -> dict:
+    """The acceptance measures against the fp32-weight oracle (norms of the
+    bf16-decoded activations and of the fp32 weights)."""
+    torch = torch_cuda()
+    if C_ref is None:
+        C_ref = oracle.gemm_f32w(A_bits, W, K)
+    an = acceptance.row_norms(oracle.bf16_decode(A_bits), K)
+    wn = acceptance.row_norms(np.asarray(W, dtype=np.float64), K)
+    odt = "bf16" if C.dtype == torch.bfloat16 else "f32"
+    return acceptance.assess(to_f64(C), C_ref, an, wn, odt)

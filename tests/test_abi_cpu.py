@@ -299,3 +299,75 @@ def test_python_dtype_guard():
         skg.skinny_gemm_bf16(a, b)
     with pytest.raises(TypeError):
         skg.skinny_gemm_bf16(b[:2], a)
+
+
+# --- fp32 weights -------------------------------------------------------------
+
+def _call_f32w(A=FAKE, W=FAKE, C=FAKE, M=4, N=256, K=7168, lda=7168, ldw=7168, ldc=256, odt=0):
+    return _capi.lib().skinny_gemm_f32w(A, W, C, M, N, K, lda, ldw, ldc, odt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=17), skg.SKG_ERR_UNSUPPORTED),
+    (dict(ldw=100), skg.SKG_ERR_INVALID_ARG),
+    (dict(W=0), skg.SKG_ERR_INVALID_ARG),
+    (dict(W=FAKE + 4), skg.SKG_ERR_MISALIGNED),
+    (dict(ldw=7170), skg.SKG_ERR_MISALIGNED),   # rows not 16-byte aligned
+    (dict(lda=7172), skg.SKG_ERR_MISALIGNED),
+])
+def test_f32w_argument_errors(kw, code):
+    assert _call_f32w(**kw) == code
+
+
+def test_f32w_row_stride_multiple_of_4_is_accepted_by_the_checks():
+    # ldw = 7172 (a multiple of 4, not of 8) passes the argument checks; with
+    # M = 0 nothing is launched
+    assert _call_f32w(M=0, ldw=7172) == skg.SKG_OK
+
+
+def test_f32w_dispatch_is_valu_and_valid():
+    for M in range(1, 17):
+        for K in (1, 7, 8, 9, 1000, 2880, 7168):
+            for N in (1, 3, 256, 384, 2112):
+                cfg = skg.skinny_gemm_f32w_dispatch(M, K, N)
+                assert cfg.inner in (skg.SKG_INNER_VALU, skg.SKG_INNER_VALU_GA), (M, K, N, cfg)
+                assert skg.skinny_gemm_f32w_check_config(M, K, N, cfg), (M, K, N, cfg)
+                assert skg.skinny_gemm_f32w_dispatch(M, K, N) == cfg
+
+
+def test_f32w_rejects_matrix_core_configs():
+    mk = _capi.SkgConfig.make
+    for inner in (skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA, skg.SKG_INNER_MFMA_RING,
+                  skg.SKG_INNER_MFMA_RING_GA):
+        cfg = mk(inner=inner, split_k=2, row_tiles=1, waves_n=1, waves_k=2, depth=2)
+        assert skg.skinny_gemm_check_config(16, 7168, 256, cfg)
+        assert not skg.skinny_gemm_f32w_check_config(16, 7168, 256, cfg)
+    for (rt, d) in _capi.VALU_VARIANTS:
+        cfg = mk(inner=skg.SKG_INNER_VALU, row_tiles=rt, depth=d, waves_k=2)
+        assert skg.skinny_gemm_f32w_check_config(4, 1024, 512, cfg)
+
+
+def test_f32w_warmup_keys():
+    shapes = [(7168, 256), (7168, 384)]
+    ms = [1, 2, 3, 4, 8, 16]
+    want = []
+    for K, N in shapes:
+        for M in ms:
+            c = skg.skinny_gemm_f32w_dispatch(M, K, N)
+            if c not in want:
+                want.append(c)
+    assert skg.skinny_gemm_f32w_warmup_keys(shapes, ms) == want
+
+
+def test_f32w_spilling_variants_are_not_built():
+    """Over fp32 weights the (M, rows, depth) combinations whose registers
+    would spill are absent (checked per M), while the bf16 kernels exist."""
+    mk = _capi.SkgConfig.make
+    lds = mk(inner=skg.SKG_INNER_VALU, row_tiles=4, depth=4, waves_k=2)
+    assert skg.skinny_gemm_f32w_check_config(8, 1024, 512, lds)
+    assert not skg.skinny_gemm_f32w_check_config(9, 1024, 512, lds)
+    assert skg.skinny_gemm_check_config(16, 1024, 512, lds)
+    ga = mk(inner=skg.SKG_INNER_VALU_GA, row_tiles=2, depth=4, waves_k=2)
+    assert skg.skinny_gemm_f32w_check_config(7, 1024, 512, ga)
+    assert not skg.skinny_gemm_f32w_check_config(8, 1024, 512, ga)
+    assert skg.skinny_gemm_check_config(8, 1024, 512, ga)
