@@ -44,6 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (weight read) and µs/call, bf16 skinny GEMM, M=1..16"
+METRIC_F32W = ("achieved HBM GB/s (weight read) and µs/call, router GEMM over fp32 weights "
+               "(bf16 activations), M=1..16")
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30  # footprint between two uses of one weight copy
@@ -52,7 +54,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # what the counters depend on: the kernels' code (the configuration they were
 # taken with is stored beside them and compared separately)
 KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
-                  "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_api.cpp"]
+                  "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_f32w_lo.hip", "skg_f32w_hi.hip",
+                  "skg_f32w_ga.hip", "skg_api.cpp"]
 F32W_SUFFIX = "_w32"  # point names of the fp32-weight router GEMM
 
 
@@ -477,7 +480,8 @@ def main():
         import oracle
         cpu = cpu_baseline(oracle, pts, bpool, args.cpu_seconds)
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC_F32W if any(p.f32w for p in pts) else METRIC,
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if any(p.f32w for p in pts) else "bf16",
