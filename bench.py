@@ -19,9 +19,12 @@ Prints ONE JSON line:
                  of the timed region;
   cpu_baseline = the CPU oracle timed on this host over the same workload.
 ``--workload router_f32w`` measures the router GEMM over fp32 weights
-(skinny_gemm_f32w; weight bytes 4*N*K) the same way.
-``--points-out FILE`` also writes, for every one of the 29 workload points
-and the 12 fp32-weight router points,
+(skinny_gemm_f32w; weight bytes 4*N*K) the same way, ``--workload mid_m`` the
+middle tier (16 < M <= 64) on the projection shapes.
+``--points-out FILE`` also writes, for every one of the 29 workload points,
+the 12 fp32-weight router points and the 12 middle-tier points, the library
+GEMM's time for the same
+product (torch.nn.functional.linear: hipBLASLt), and
 the kernel time per call (median of 200 dispatch-recorded event pairs), the
 time per call eager, from HIP-graph replay and with one hot weight copy, the
 streaming-read ceiling for the same weight bytes, and the CPU oracle on all
@@ -205,6 +208,38 @@ def time_points_graph(torch, lib, pts, stream, calls=200, warm=20):
     return res
 
 
+def time_library_graph(torch, pts, stream, calls=200, warm=20):
+    """us per call of the library GEMM a caller would otherwise use for the
+    same product (torch.nn.functional.linear, i.e. hipBLASLt: bf16 in, bf16
+    out; over fp32 weights, the fp32 GEMM of the widened activations), timed
+    like time_points_graph: back-to-back calls over the rotating weight
+    copies, replayed from a HIP graph."""
+    F = torch.nn.functional
+    res = {}
+    for pt in pts:
+        A = pt.A.float() if pt.f32w else pt.A
+        with torch.cuda.stream(stream):
+            for _ in range(warm):
+                F.linear(A, next_copy(pt))
+        torch.cuda.synchronize()
+        n = min(calls, 4 * len(pt.copies["list"])) if pt.weight_bytes > (64 << 20) else calls
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                F.linear(A, next_copy(pt))
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        res[pt.name()] = e0.elapsed_time(e1) * 1000.0 / n
+        del g
+    return res
+
+
 def time_points_eager(torch, lib, pts, stream, calls=200, warm=20):
     res = {}
     h = stream.cuda_stream
@@ -277,7 +312,8 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
     zero-fill kernel) that marks them in a kernel trace, so a rocprofv3
     kernel trace of this run can be attributed to points by order."""
     h = stream.cuda_stream
-    spec = inputs.all_points() + inputs.WORKLOADS_F32W["router_f32w"]
+    spec = (inputs.all_points() + inputs.WORKLOADS_F32W["router_f32w"] +
+            inputs.WORKLOADS_MID["mid_m"])
 
     def key_of(p):
         return (p["K"], p["N"], p.get("w") == "f32")
@@ -315,6 +351,7 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
             order += 1
         eager = time_points_eager(torch, lib, ps, stream)
         graph = time_points_graph(torch, lib, ps, stream)
+        libgemm = time_library_graph(torch, ps, stream)
         # streaming-read ceiling over the same rotating weight copies
         lst = bp[(K, N, f32w)]["list"]
         nb = lst[0].element_size() * N * K
@@ -338,6 +375,8 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
             e = table[pt.name()]
             e.update({"us_per_call_eager": round(eager[pt.name()], 3),
                       "us_per_call_graph": round(graph[pt.name()], 3),
+                      "us_per_call_library_graph": round(libgemm[pt.name()], 3),
+                      "speedup_vs_library_graph": round(libgemm[pt.name()] / graph[pt.name()], 3),
                       "us_per_call_hot_graph": round(hot_us[pt.name()], 3),
                       "read_ceiling_us_eager": round(read_us, 3)})
             k_us = e["kernel_us_events_median"]
@@ -393,7 +432,7 @@ def main():
         print("bench.py: libskinny_gemm.so has no gfx950 device/code to run", file=sys.stderr)
         sys.exit(1)
 
-    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_F32W)
+    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_F32W, **inputs.WORKLOADS_MID)
     workload = groups[args.workload]
     if args.only:
         M, K, N = (int(x) for x in args.only.split(","))

@@ -1,7 +1,7 @@
 /*
  * skinny_gemm.h -- C ABI of the MI355X (gfx950) small-M bf16 "skinny" GEMM.
  *
- *     C[m, n] = sum_k A[m, k] * B[n, k]          (C = A . B^T, M <= 16)
+ *     C[m, n] = sum_k A[m, k] * B[n, k]          (C = A . B^T, M <= 64)
  *
  * A (activations, M x K) and B (weights, N x K) are row-major bf16; the sum
  * is accumulated in fp32; C is written as fp32 or as bf16 (round to nearest
@@ -20,7 +20,12 @@
  *     关键源码片段 (dispatch and get_warmup_keys).
  *   - PR #48597 page ("GLM-5.2 Blackwell decode optimizations"), section
  *     实现拆解 item 3 and the key-file list: bf16_skinny_gemm for the qkv_a /
- *     q_b / eh_proj decode projections, with a strided-output test.
+ *     q_b / eh_proj decode projections, with a strided-output test; the same
+ *     item chooses among a skinny GEMM for small M, a fused GEMM for middle
+ *     M and the library GEMM for large M by measured per-shape thresholds.
+ *     Here M <= 16 is the skinny tier and 16 < M <= 64 the middle tier (the
+ *     matrix-core kernels with 2 to 4 tiles of 16 tokens);
+ *     skinny_gemm_max_m gives the measured crossover to the library GEMM.
  *
  * Conventions shared by every entry point:
  *   - Pointers A, B, C are DEVICE pointers owned by the caller; the library
@@ -52,7 +57,8 @@ typedef enum {
     SKG_OK = 0,
     SKG_ERR_INVALID_ARG = 1, /* null pointer with non-zero size, negative size,
                                 lda < K, ldb < K, ldc < N, bad out_dtype, bad config */
-    SKG_ERR_UNSUPPORTED = 2, /* M > 16: the caller should use another GEMM */
+    SKG_ERR_UNSUPPORTED = 2, /* M > 64 (M > 16 over fp32 weights): the caller
+                                should use another GEMM */
     SKG_ERR_MISALIGNED = 3,  /* A or B not 16-byte aligned, lda or ldb not a
                                 multiple of 8, C not aligned to its element size */
     SKG_ERR_NOT_WARMED = 4,  /* the stream is capturing a graph and its split-K
@@ -87,7 +93,8 @@ typedef enum {
 typedef enum {
     SKG_INNER_VALU = 0,    /* bf16 dot2 instructions, 16 lanes per row of B;
                               A staged in LDS */
-    SKG_INNER_MFMA = 1,    /* 16x16x32 bf16 matrix-core tiles (M padded to 16);
+    SKG_INNER_MFMA = 1,    /* 16x16x32 bf16 matrix-core tiles (M padded to a
+                              multiple of 16, up to 64);
                               A staged in LDS */
     SKG_INNER_MFMA_GA = 2, /* as SKG_INNER_MFMA, with the activation fragments
                               read from global memory (L2) each K step: no LDS
@@ -104,7 +111,8 @@ typedef enum {
                                    into the LDS ring */
 } skg_inner;
 
-#define SKG_MAX_M 16
+#define SKG_MAX_M 64      /* the matrix-core kinds; the VALU kinds take M <= 16 */
+#define SKG_MAX_M_VALU 16
 
 /* A kernel configuration: what skinny_gemm_dispatch returns and what
  * skinny_gemm_bf16_with_config accepts.  Plain data; compare field by field. */
@@ -134,7 +142,7 @@ typedef struct skg_config {
  *   B: device bf16 [N, ldb], 16-byte aligned, ldb % 8 == 0, ldb >= K.
  *   C: device [M, ldc] of fp32 (out_dtype SKG_OUT_F32, 4-byte aligned) or
  *      bf16 (SKG_OUT_BF16, 2-byte aligned, round to nearest even), ldc >= N.
- *   0 <= M <= 16 (M > 16 -> SKG_ERR_UNSUPPORTED), N >= 0, K >= 0.
+ *   0 <= M <= 64 (M > 64 -> SKG_ERR_UNSUPPORTED), N >= 0, K >= 0.
  *   M == 0 or N == 0: nothing is written, SKG_OK.  K == 0: C gets zeros.
  * The result for a given (M, K, N) and inputs is bit-identical from call to
  * call (fixed summation order; no floating-point atomics).
@@ -161,7 +169,7 @@ int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M,
                                  const skg_config *cfg);
 
 /* The configuration used for (M, K, N).  Pure host function: no GPU access,
- * deterministic, the same answer on every call.  M must be in 1..16,
+ * deterministic, the same answer on every call.  M must be in 1..64,
  * K >= 0, N >= 1; otherwise SKG_ERR_INVALID_ARG / SKG_ERR_UNSUPPORTED. */
 int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
 
@@ -243,6 +251,11 @@ int skinny_gemm_f32w_warmup_keys(const int *kn_pairs, int n_shapes,
 int skinny_gemm_f32w_warmup(const int *kn_pairs, int n_shapes, const int *m_values,
                             int n_m, void *stream, int *n_configs_out);
 
+/* The hipError_t value behind this thread's most recent SKG_ERR_HIP from a
+ * GEMM call, zero-fill or streaming read (0 if there was none): a launch
+ * failure reports the runtime's own code here. */
+int skinny_gemm_last_hip_error(void);
+
 /* 1 if a gfx950 device is current and the library's kernels load, else 0. */
 int skinny_gemm_available(void);
 
@@ -256,6 +269,18 @@ int skinny_gemm_available(void);
    bandwidth figures are compared with.  `src` 16-byte aligned and `bytes` a
    multiple of 16 (else SKG_ERR_MISALIGNED); bytes == 0 is a no-op. */
 int skinny_gemm_stream_read(const void *src, size_t bytes, void *sink, void *stream);
+
+/*
+ * The measured crossover of the tiers for (K, N): *max_m receives the largest
+ * M for which this library was measured faster than the library GEMM
+ * (hipBLASLt through torch.nn.functional.linear, both timed as back-to-back
+ * calls from a HIP graph over weight copies rotated past the Infinity Cache)
+ * at every measured M up to it; a caller uses skinny_gemm_bf16 for
+ * M <= *max_m and the library GEMM above.  Shapes that were not measured get
+ * SKG_MAX_M_VALU.  Pure host.  (The pages' skinny_max threshold per (N, K),
+ * PR #48597 page, section 实现拆解 item 3.)
+ */
+int skinny_gemm_max_m(int K, int N, int *max_m);
 
 /* Static description of a status code. */
 const char *skinny_gemm_strerror(int status);

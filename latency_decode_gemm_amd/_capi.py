@@ -33,7 +33,8 @@ SKG_INNER_MFMA_GA = 2
 SKG_INNER_VALU_GA = 3
 SKG_INNER_MFMA_RING = 4
 SKG_INNER_MFMA_RING_GA = 5
-SKG_MAX_M = 16
+SKG_MAX_M = 64
+SKG_MAX_M_VALU = 16
 
 # Compiled (row_tiles, depth) pairs per inner product (the library's tables).
 VALU_VARIANTS = ((1, 4), (1, 8), (1, 12), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4))
@@ -102,6 +103,8 @@ SIGNATURES = {
     "skinny_gemm_f32w_check_config": (_i, [_i, _i, _i, _cfgp]),
     "skinny_gemm_f32w_warmup_keys": (_i, [_ip, _i, _ip, _i, _cfgp, _i, _ip]),
     "skinny_gemm_f32w_warmup": (_i, [_ip, _i, _ip, _i, _vp, _ip]),
+    "skinny_gemm_max_m": (_i, [_i, _i, _ip]),
+    "skinny_gemm_last_hip_error": (_i, []),
     "skinny_gemm_available": (_i, []),
     "skinny_gemm_stream_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
     "skinny_gemm_strerror": (ctypes.c_char_p, [_i]),
@@ -121,6 +124,16 @@ def lib() -> ctypes.CDLL:
                     raise RuntimeError(
                         f"{LIB_PATH} is missing: build it with "
                         "`python -m latency_decode_gemm_amd.build` (there is no fallback)")
+                # The library needs the HIP runtime that torch, whose device
+                # memory and streams it is handed, already uses: with torch
+                # loaded first, the library's libamdhip64.so.7 dependency
+                # resolves to torch's copy; loaded before it, the library
+                # would bind the system runtime and the process would hold
+                # two runtimes that do not share streams or loaded kernels.
+                try:
+                    import torch  # noqa: F401
+                except ImportError:
+                    pass
                 dll = ctypes.CDLL(LIB_PATH)
                 for name, (res, args) in SIGNATURES.items():
                     fn = getattr(dll, name)
@@ -168,6 +181,8 @@ class SkinnyGemmError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = lib().skinny_gemm_strerror(status).decode()
+        if status == SKG_ERR_HIP:
+            msg += f", hipError_t {lib().skinny_gemm_last_hip_error()}"
         super().__init__(f"{where}: status {status} ({msg})")
 
 

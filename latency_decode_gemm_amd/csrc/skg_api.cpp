@@ -38,6 +38,12 @@ struct TableEntry {
 #include "tuned_table.inc"
 #include "tuned_table_f32w.inc"
 
+struct CrossoverEntry {
+    int K, N, max_m;
+};
+
+#include "crossover_table.inc"
+
 constexpr int kNumTable = sizeof(kTunedTable) / sizeof(kTunedTable[0]);
 constexpr int kNumTableF32w = sizeof(kTunedTableF32w) / sizeof(kTunedTableF32w[0]);
 
@@ -52,18 +58,21 @@ bool config_equal(const skg_config &a, const skg_config &b) {
 }
 
 // Default for shapes the table does not list: VALU up to M = 8, MFMA above
-// (fp32 weights: VALU throughout); 4 waves per workgroup (2 on rows x 2 on
-// K); K split only when the staged A slice would exceed 64 KB or the row
-// blocks cannot cover the 256 CUs; each workgroup then streams enough row
-// blocks to keep the grid near 512.
+// (fp32 weights: VALU throughout; above 16 tokens the LDS-ring MFMA kernel,
+// depth 2, one K-wave); 4 waves per workgroup (2 on rows x 2 on K); K split
+// only when the staged A slice would exceed 64 KB or the row blocks cannot
+// cover the 256 CUs; each workgroup then streams enough row blocks to keep
+// the grid near 512.
 skg_config default_config(int M, int K, int N, bool f32w = false) {
     skg_config c;
     std::memset(&c, 0, sizeof c);
-    c.inner = (M > 8 && !f32w) ? SKG_INNER_MFMA_GA : SKG_INNER_VALU;
+    c.inner = (M > 16 && !f32w)  ? SKG_INNER_MFMA_RING_GA
+              : (M > 8 && !f32w) ? SKG_INNER_MFMA_GA
+                                 : SKG_INNER_VALU;
     c.row_tiles = (c.inner == SKG_INNER_VALU) ? 2 : 1;
-    c.depth = 4;
+    c.depth = (M > 16) ? 2 : 4;
     c.waves_n = 2;
-    c.waves_k = 2;
+    c.waves_k = (M > 16) ? 1 : 2;
     const int rows_per_wg = (c.inner == SKG_INNER_VALU ? 4 * c.row_tiles : 16) * c.waves_n;
     const int num_rb = ceil_div(std::max(N, 1), rows_per_wg);
     const int nck = ceil_div(K, kChunk);
@@ -86,6 +95,16 @@ skg_config default_config(int M, int K, int N, bool f32w = false) {
     // the stash holds rb_per_wg row blocks: more workgroups if it does not fit
     while (!make_geometry(M, K, N, c, &g) && c.rb_per_wg > 1) c.rb_per_wg /= 2;
     return c;
+}
+
+// The HIP error behind this thread's last SKG_ERR_HIP (hipSuccess if none).
+thread_local int g_last_hip_error = 0;
+
+// SKG_OK if e is hipSuccess, else records e and returns SKG_ERR_HIP.
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SKG_OK;
+    g_last_hip_error = (int)e;
+    return SKG_ERR_HIP;
 }
 
 struct Workspace {
@@ -144,7 +163,7 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
 int check_args(const void *A, const void *B, const void *C, int M, int N, int K, int64_t lda,
                int64_t ldb, int64_t ldc, int out_dtype, bool f32w = false) {
     if (M < 0 || N < 0 || K < 0) return SKG_ERR_INVALID_ARG;
-    if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
+    if (M > (f32w ? kMaxMValu : SKG_MAX_M)) return SKG_ERR_UNSUPPORTED;
     if (out_dtype != SKG_OUT_F32 && out_dtype != SKG_OUT_BF16) return SKG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return SKG_OK;
     if (lda < K || ldb < K || ldc < N) return SKG_ERR_INVALID_ARG;
@@ -167,10 +186,8 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     hipEvent_t start = reinterpret_cast<hipEvent_t>(start_v);
     hipEvent_t stop = reinterpret_cast<hipEvent_t>(stop_v);
     if (K == 0) {
-        return launch_zero_fill(C, M, N, ldc, out_dtype == SKG_OUT_BF16, stream, start, stop) ==
-                       hipSuccess
-                   ? SKG_OK
-                   : SKG_ERR_HIP;
+        return hip_status(launch_zero_fill(C, M, N, ldc, out_dtype == SKG_OUT_BF16, stream, start,
+                                           stop));
     }
     KParams p;
     std::memset(&p, 0, sizeof p);
@@ -186,7 +203,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.out_bf16 = (out_dtype == SKG_OUT_BF16);
     p.w_f32 = f32w ? 1 : 0;
     if (K < kChunk)  // rows shorter than one 16-byte window
-        return launch_small_k(p, stream, start, stop) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
+        return hip_status(launch_small_k(p, stream, start, stop));
     Geometry g;
     if (!make_geometry(M, K, N, cfg, &g)) return SKG_ERR_INVALID_ARG;
     if (f32w && !variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, true, M))
@@ -213,7 +230,7 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
         p.ws = w.ws;
         p.tickets = w.tickets;
     }
-    return launch(p, g, cfg, stream, start, stop) == hipSuccess ? SKG_OK : SKG_ERR_HIP;
+    return hip_status(launch(p, g, cfg, stream, start, stop));
 }
 
 }  // namespace
@@ -237,7 +254,9 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     const bool valu = cfg.inner == SKG_INNER_VALU || cfg.inner == SKG_INNER_VALU_GA;
     // VALU_GA keeps depth x M activation chunks in registers
     if (cfg.inner == SKG_INNER_VALU_GA && (M > 8 || M * cfg.depth > 32)) return false;
-    if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth)) return false;
+    if (valu && M > kMaxMValu) return false;
+    if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, false, M)) return false;
+    const int mt = (M + 15) / 16;  // MFMA token tiles of 16
     if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
     if (cfg.rb_per_wg < 1) return false;
     Geometry r;
@@ -270,17 +289,18 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (cfg.inner == SKG_INNER_VALU)
         a_bytes = (size_t)M * r.lds_stride * 2;
     else if (lds_frag)
-        a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16;
+        a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16 * mt;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
-    // MFMA: one transpose tile per 16-row tile of B per wave, plus one for A (GA)
-    // (the LDS ring: depth slots of those tiles)
-    const int tiles = (valu ? 0 : lds_frag ? cfg.row_tiles : cfg.row_tiles + 1) *
+    // MFMA: one transpose tile per 16-row tile of B per wave, plus one per
+    // token tile for A (GA) (the LDS ring: depth slots of those tiles)
+    const int tiles = (valu ? 0 : lds_frag ? cfg.row_tiles : cfg.row_tiles + mt) *
                       (ring ? cfg.depth : 1);
     const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
     r.stash_offset = (int)(r.tr_offset + tr_bytes);
     // stash: every wave's partial sums of each of the workgroup's row blocks
-    // (VALU: M x its rows; MFMA: one 16 x 16 fp32 tile per 16 rows)
-    const size_t per_block = valu ? (size_t)M * r.rows_per_wg : (size_t)16 * r.rows_per_wg;
+    // (VALU: M x its rows; MFMA: one 16 x 16 fp32 tile per 16 rows and
+    // token tile)
+    const size_t per_block = valu ? (size_t)M * r.rows_per_wg : (size_t)16 * mt * r.rows_per_wg;
     const size_t blocks_per_wg = (size_t)ceil_div(r.num_rb, r.grid_rb);
     // (a row block covered by one wave is written from registers)
     // (the single-pass split-K settles row blocks workgroup by workgroup)
@@ -316,8 +336,9 @@ bool config_ok(int M, int K, int N, const skg_config &cfg, bool f32w) {
 // The tuned entry for (M, K, N), else the default rule; pure.
 int dispatch_impl(int M, int K, int N, bool f32w, skg_config *out) {
     if (!out) return SKG_ERR_INVALID_ARG;
-    if (M < 1 || K < 0 || N < 1) return M > SKG_MAX_M ? SKG_ERR_UNSUPPORTED : SKG_ERR_INVALID_ARG;
-    if (M > SKG_MAX_M) return SKG_ERR_UNSUPPORTED;
+    const int max_m = f32w ? kMaxMValu : SKG_MAX_M;
+    if (M < 1 || K < 0 || N < 1) return M > max_m ? SKG_ERR_UNSUPPORTED : SKG_ERR_INVALID_ARG;
+    if (M > max_m) return SKG_ERR_UNSUPPORTED;
     const TableEntry *table = f32w ? kTunedTableF32w : kTunedTable;
     const int n = f32w ? kNumTableF32w : kNumTable;
     for (int i = 0; i < n; ++i) {
@@ -552,16 +573,24 @@ int skinny_gemm_f32w_warmup(const int *kn_pairs, int n_shapes, const int *m_valu
     return warmup_impl(true, kn_pairs, n_shapes, m_values, n_m, stream_v, n_configs_out);
 }
 
+int skinny_gemm_max_m(int K, int N, int *max_m) {
+    if (!max_m || K < 0 || N < 1) return SKG_ERR_INVALID_ARG;
+    *max_m = SKG_MAX_M_VALU;
+    for (const CrossoverEntry &e : kCrossover)
+        if (e.K == K && e.N == N && e.max_m > 0) *max_m = e.max_m;
+    return SKG_OK;
+}
+
 int skinny_gemm_stream_read(const void *src, size_t bytes, void *sink, void *stream) {
     if (bytes == 0) return SKG_OK;
     if (src == nullptr || sink == nullptr) return SKG_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(src) & 15u) || (bytes & 15u)) return SKG_ERR_MISALIGNED;
     if (reinterpret_cast<uintptr_t>(sink) & 3u) return SKG_ERR_MISALIGNED;
-    return launch_stream_read(src, bytes / 16, sink, reinterpret_cast<hipStream_t>(stream)) ==
-                   hipSuccess
-               ? SKG_OK
-               : SKG_ERR_HIP;
+    return hip_status(
+        launch_stream_read(src, bytes / 16, sink, reinterpret_cast<hipStream_t>(stream)));
 }
+
+int skinny_gemm_last_hip_error(void) { return g_last_hip_error; }
 
 int skinny_gemm_available(void) {
     int n = 0;

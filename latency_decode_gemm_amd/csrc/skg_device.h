@@ -655,15 +655,18 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 // as (partial) zeros by ordinary LDS stores.
 // (RAW: through lds_dma16_raw, for kernels whose other LDS writes by DMA the
 // compiler does not see either; their barrier waits for these loads)
-template <bool RAW = false>
+// MT token tiles of 16 (M up to 16 MT): the 1 KB blocks of one 32-wide step
+// follow each other, tile mt holding tokens 16 mt .. 16 mt + 15.
+template <bool RAW = false, int MT = 1>
 __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int wg_c0) {
     const int lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
-    const int m = min(lane & 15, p.M - 1);
-    const uint16_t *rowp = p.A + (int64_t)m * p.lda;
-    const int nblk = p.wg_chunks >> 2;  // 32-wide steps
+    const int nblk = (p.wg_chunks >> 2) * MT;  // (32-wide step, token tile) blocks
     for (int blk = threadIdx.x >> 6; blk < nblk; blk += nwaves) {
-        const int c = wg_c0 + 4 * blk + (lane >> 4);
+        const int mt = blk % MT;
+        const int m = min(16 * mt + (lane & 15), p.M - 1);
+        const uint16_t *rowp = p.A + (int64_t)m * p.lda;
+        const int c = wg_c0 + 4 * (blk / MT) + (lane >> 4);
         uint16_t *dst = As + blk * 64 * kChunk;
         if (c < p.nfull) {
             if constexpr (RAW)
@@ -688,15 +691,17 @@ __device__ __forceinline__ int tile_slot(int r, int c) { return r * 16 + (c ^ r)
 
 // G: 16-row tiles per wave; PF: 128-wide K steps of loads in flight; AQ: 0
 // when the activations are staged in LDS, else the number of activation loads
-// per step (rows 4q + (lane >> 4), q < AQ: AQ = 4 covers M <= 16, AQ = 2
-// covers M <= 8): the activations are then loaded from global memory
-// (L2-resident), in the same ring and row-segment layout as B, and transposed
-// through their own wave-private tile.  M <= 16 at run time (activation rows
-// m >= M are fed as zeros).
-template <int G, int PF, int AQ>
+// per step and token tile (rows 4q + (lane >> 4), q < AQ: AQ = 4 covers 16
+// tokens, AQ = 2 covers M <= 8): the activations are then loaded from global
+// memory (L2-resident), in the same ring and row-segment layout as B, and
+// transposed through their own wave-private tiles.  MT: token tiles of 16
+// (M <= 16 MT at run time; MT > 1 takes AQ = 4), each its own 16-row MFMA
+// operand against the same B tiles.  Activation rows m >= M are fed as zeros.
+template <int G, int PF, int AQ, int MT = 1>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     constexpr bool AG = AQ > 0;
-    constexpr int NA = AG ? AQ : 1;
+    static_assert(MT == 1 || AQ == 0 || AQ == 4, "several token tiles load whole tiles");
+    constexpr int NA = AG ? MT * AQ : 1;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
@@ -715,9 +720,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     const int T = w.nblk * SPB;
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
     const int tail_st = max(0, (p.nfull - wv_c0) / kValuStep);
-    constexpr int NT = G + (AG ? 1 : 0);  // transpose tiles per wave (B tiles, then A)
+    constexpr int NT = G + (AG ? MT : 0);  // transpose tiles per wave (B tiles, then A)
     uint4 *tile = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (NT * 256);
-    // AG: activation rows 4q + hi of this lane (rows >= M read row M-1, masked)
+    // AG: activation rows 4q + hi of this lane, A tile q / 4 (rows >= M read
+    // row M-1, masked)
     const uint16_t *arow[NA];
     uint4 amask[NA];
 #pragma unroll
@@ -750,7 +756,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             for (int q = 0; q < 4; ++q) dst[t][q] = ldg16_stream(rowp[t][q] + off);
         if constexpr (AG)
 #pragma unroll
-            for (int q = 0; q < AQ; ++q) adst[q] = ldg16(arow[q] + off);
+            for (int q = 0; q < NA; ++q) adst[q] = ldg16(arow[q] + off);
         if (++lst == SPB) {
             lst = 0;
             set_rows(++lb);
@@ -760,7 +766,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     uint4 buf[PF][G][4];
     uint4 abuf[PF][NA];
     set_rows(0);
-    if constexpr (!AG) stage_a_frag(p, As, w.wg_c0);  // oldest loads, as in the VALU kernel
+    if constexpr (!AG) stage_a_frag<false, MT>(p, As, w.wg_c0);  // oldest loads, as in the VALU kernel
 #pragma unroll
     for (int i = 0; i < PF; ++i) issue(buf[i], abuf[i]);
 
@@ -773,18 +779,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             tile[G * 256 + tile_slot(4 * q + hi, lo)] = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    f32x4_t acc[G];
+    f32x4_t acc[G][MT];
 #pragma unroll
-    for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // LDS activation fragments of this wave: one 1 KB block per 32-wide step;
+    // LDS activation fragments of this wave: MT 1 KB blocks per 32-wide step;
     // lanes of tokens m >= M zero what they read
-    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
-    const uint32_t lane_mask = (lo < M) ? 0xFFFFFFFFu : 0u;
-    // stash: [row block][K-wave][N-wave][tile] blocks of 64 lanes x 4 floats;
-    // lane 16*hi + lo, element v holds token 4*hi + v, row 16*tile + lo
-    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * 64 + lane;
-    const int st_block = p.waves_k * p.waves_n * G * 64;  // f32x4 per row block
+    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * MT * 64 + lane) * kChunk;
+    uint32_t lane_mask[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) lane_mask[mt] = (16 * mt + lo < M) ? 0xFFFFFFFFu : 0u;
+    // stash: [row block][K-wave][N-wave][tile][token tile] blocks of 64 lanes x
+    // 4 floats; lane 16*hi + lo, element v holds token 16*mt + 4*hi + v, row
+    // 16*tile + lo
+    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * MT * 64 + lane;
+    const int st_block = p.waves_k * p.waves_n * G * MT * 64;  // f32x4 per row block
     const bool direct = direct_write(p);
     const int rlw = wn * (16 * G);  // first local row of this wave
 
@@ -807,26 +818,32 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             for (int q = 0; q < 4; ++q) tile[t * 256 + tile_slot(4 * q + hi, lo)] = bv[t][q];
         if constexpr (AG)
 #pragma unroll
-            for (int q = 0; q < AQ; ++q)
-                tile[G * 256 + tile_slot(4 * q + hi, lo)] = and4(av[q], amask[q]);
+            for (int q = 0; q < NA; ++q)
+                tile[(G + q / 4) * 256 + tile_slot(4 * (q % 4) + hi, lo)] = and4(av[q], amask[q]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint4 a;
-            if constexpr (AG) {
-                a = tile[G * 256 + tile_slot(lo, 4 * s + hi)];
-            } else {
-                a = lds16(ap + (cst * 4 + s) * (64 * kChunk));
-                a.x &= lane_mask;
-                a.y &= lane_mask;
-                a.z &= lane_mask;
-                a.w &= lane_mask;
+            bf16x8_t a8[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint4 a;
+                if constexpr (AG) {
+                    a = tile[(G + mt) * 256 + tile_slot(lo, 4 * s + hi)];
+                } else {
+                    a = lds16(ap + ((cst * 4 + s) * MT + mt) * (64 * kChunk));
+                    a.x &= lane_mask[mt];
+                    a.y &= lane_mask[mt];
+                    a.z &= lane_mask[mt];
+                    a.w &= lane_mask[mt];
+                }
+                a8[mt] = __builtin_bit_cast(bf16x8_t, a);
             }
-            const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
                 const uint4 b8 = tile[t * 256 + tile_slot(lo, 4 * s + hi)];
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a8, __builtin_bit_cast(bf16x8_t, b8), acc[t], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a8[mt], __builtin_bit_cast(bf16x8_t, b8), acc[t][mt], 0, 0, 0);
             }
         }
         if (++cst == SPB) {
@@ -836,27 +853,31 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             block_rows(p, rb, bst, bcnt);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
-                if (!direct) {
-                    st[cb * st_block + t * 64] = acc[t];
-                } else {
-                    // lane index re-derived here so the compiler cannot keep
-                    // the store addresses live across the whole stream
-                    int ln = lane;
-                    __asm__ volatile("" : "+v"(ln));
-                    const int rl = rlw + 16 * t + (ln & 15);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * (ln >> 4) + v;
-                        if (m < M) {
-                            if (p.split_k == 1) {
-                                if (rl < bcnt) store_c(p, m, bst + rl, acc[t][v]);
-                            } else {
-                                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (!direct) {
+                        st[cb * st_block + (t * MT + mt) * 64] = acc[t][mt];
+                    } else {
+                        // lane index re-derived here so the compiler cannot
+                        // keep the store addresses live across the whole stream
+                        int ln = lane;
+                        __asm__ volatile("" : "+v"(ln));
+                        const int rl = rlw + 16 * t + (ln & 15);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int m = 16 * mt + 4 * (ln >> 4) + v;
+                            if (m < M) {
+                                if (p.split_k == 1) {
+                                    if (rl < bcnt) store_c(p, m, bst + rl, acc[t][mt][v]);
+                                } else {
+                                    p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] =
+                                        acc[t][mt][v];
+                                }
                             }
                         }
                     }
+                    acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
-                acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
             cst = 0;
             ++cb;
@@ -880,9 +901,9 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             [&](int b, int q, int rl) {
                 const int wq = rl / (16 * G);  // N-wave
                 const int t = (rl >> 4) % G;   // tile
-                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + (rl & 15) * 4;
+                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * MT * 256 + (rl & 15) * 4;
             },
-            [&](int m) { return 64 * (m >> 2) + (m & 3); });
+            [&](int m) { return 256 * (m >> 4) + 64 * ((m & 15) >> 2) + (m & 3); });
 }
 
 // ---- MFMA kernel with an LDS ring --------------------------------------------
@@ -898,11 +919,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 // operands as they are read.  Tokens m >= M read row M - 1 of A and produce
 // accumulator rows that are never stored (an MFMA output row depends on its
 // own activation row only).
-template <int G, int PF, int AQ>
+template <int G, int PF, int AQ, int MT = 1>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p) {
     constexpr bool AG = AQ > 0;
-    constexpr int NT = G + (AG ? 1 : 0);  // tiles per ring slot
-    constexpr int L = 4 * G + AQ;         // loads per K step
+    static_assert(MT == 1 || AQ == 0 || AQ == 4, "several token tiles load whole tiles");
+    constexpr int NT = G + (AG ? MT : 0);  // tiles per ring slot
+    constexpr int L = 4 * G + MT * AQ;     // loads per K step
     static_assert((PF - 1) * L < 64 && PF * L < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
@@ -927,9 +949,9 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     int swz[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) swz[q] = lo ^ (4 * q + hi);
-    const uint16_t *arow[AG ? AQ : 1];
+    const uint16_t *arow[AG ? MT * AQ : 1];
 #pragma unroll
-    for (int q = 0; q < (AG ? AQ : 1); ++q)
+    for (int q = 0; q < (AG ? MT * AQ : 1); ++q)
         arow[q] = p.A + (int64_t)min(4 * q + hi, M - 1) * p.lda;
 
     int lb = 0, lst = 0;
@@ -957,7 +979,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
             for (int t = 0; t < G; ++t)
                 lds_dma16_raw<true>(rowp[t][q] + off, dst + t * kTileBytes + 1024 * q);
             if constexpr (AG)
-                if (q < AQ) lds_dma16_raw<false>(arow[q] + off, dst + G * kTileBytes + 1024 * q);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (q < AQ)
+                        lds_dma16_raw<false>(arow[mt * AQ + q] + off,
+                                             dst + (G + mt) * kTileBytes + 1024 * q);
         }
         if (++lst == SPB) {
             lst = 0;
@@ -966,17 +992,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     };
 
     set_rows(0);
-    if constexpr (!AG) stage_a_frag<true>(p, As, w.wg_c0);  // oldest loads
+    if constexpr (!AG) stage_a_frag<true, MT>(p, As, w.wg_c0);  // oldest loads
 #pragma unroll
     for (int i = 0; i < PF; ++i) issue(i);
     if constexpr (!AG) staged_barrier<PF * L>();
 
-    f32x4_t acc[G];
+    f32x4_t acc[G][MT];
 #pragma unroll
-    for (int t = 0; t < G; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * 64 + lane) * kChunk;
-    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * 64 + lane;
-    const int st_block = p.waves_k * p.waves_n * G * 64;
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *ap = As + ((wk * p.wave_chunks) / 4 * MT * 64 + lane) * kChunk;
+    f32x4_t *st = reinterpret_cast<f32x4_t *>(stash) + (wk * p.waves_n + wn) * G * MT * 64 + lane;
+    const int st_block = p.waves_k * p.waves_n * G * MT * 64;
     const bool direct = direct_write(p);
     const int rlw = wn * (16 * G);
 
@@ -988,11 +1016,13 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const uint4 *tl = ring + slot * (NT * 256);
         // all operands first, so the reads go out back to back
-        uint4 av[4], bv[4][G];
+        uint4 av[4][MT], bv[4][G];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            av[s] = AG ? tl[G * 256 + tile_slot(lo, 4 * s + hi)]
-                       : lds16(ap + (cst * 4 + s) * (64 * kChunk));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[s][mt] = AG ? tl[(G + mt) * 256 + tile_slot(lo, 4 * s + hi)]
+                               : lds16(ap + ((cst * 4 + s) * MT + mt) * (64 * kChunk));
 #pragma unroll
             for (int t = 0; t < G; ++t) bv[s][t] = tl[t * 256 + tile_slot(lo, 4 * s + hi)];
         }
@@ -1000,7 +1030,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const uint4 mk = tail_mask(wv_c0 + cst * kValuStep + 4 * s + hi, p);
-                av[s] = and4(av[s], mk);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) av[s][mt] = and4(av[s][mt], mk);
 #pragma unroll
                 for (int t = 0; t < G; ++t) bv[s][t] = and4(bv[s][t], mk);
             }
@@ -1009,34 +1040,42 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int t = 0; t < G; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, av[s]), __builtin_bit_cast(bf16x8_t, bv[s][t]),
-                    acc[t], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av[s][mt]),
+                        __builtin_bit_cast(bf16x8_t, bv[s][t]), acc[t][mt], 0, 0, 0);
         if (++cst == SPB) {
             const int rb = w.rb0 + cb * w.rbs;
             int bst, bcnt;
             block_rows(p, rb, bst, bcnt);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
-                if (!direct) {
-                    st[cb * st_block + t * 64] = acc[t];
-                } else {
-                    int ln = lane;
-                    __asm__ volatile("" : "+v"(ln));
-                    const int rl = rlw + 16 * t + (ln & 15);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = 4 * (ln >> 4) + v;
-                        if (m < M) {
-                            if (p.split_k == 1) {
-                                if (rl < bcnt) store_c(p, m, bst + rl, acc[t][v]);
-                            } else {
-                                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = acc[t][v];
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (!direct) {
+                        st[cb * st_block + (t * MT + mt) * 64] = acc[t][mt];
+                    } else {
+                        // lane index re-derived here so the compiler cannot
+                        // keep the store addresses live across the whole stream
+                        int ln = lane;
+                        __asm__ volatile("" : "+v"(ln));
+                        const int rl = rlw + 16 * t + (ln & 15);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int m = 16 * mt + 4 * (ln >> 4) + v;
+                            if (m < M) {
+                                if (p.split_k == 1) {
+                                    if (rl < bcnt) store_c(p, m, bst + rl, acc[t][mt][v]);
+                                } else {
+                                    p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] =
+                                        acc[t][mt][v];
+                                }
                             }
                         }
                     }
+                    acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
-                acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
             cst = 0;
             ++cb;
@@ -1059,11 +1098,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
         write_blocks(
             p, w, stash, flag,
             [&](int b, int q, int rl) {
-                const int wq = rl / (16 * G);
-                const int t = (rl >> 4) % G;
-                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * 256 + (rl & 15) * 4;
+                const int wq = rl / (16 * G);  // N-wave
+                const int t = (rl >> 4) % G;   // tile
+                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * MT * 256 + (rl & 15) * 4;
             },
-            [&](int m) { return 64 * (m >> 2) + (m & 3); });
+            [&](int m) { return 256 * (m >> 4) + 64 * ((m & 15) >> 2) + (m & 3); });
 }
 
 // Over fp32 weights the register ring is twice as large, and these

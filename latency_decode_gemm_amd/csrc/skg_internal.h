@@ -110,6 +110,13 @@ constexpr int kNumValu = sizeof(kValuVariants) / sizeof(kValuVariants[0]);
 KernelPtr valu_kernel_lo(int M, int variant);
 KernelPtr valu_kernel_hi(int M, int variant);
 KernelPtr valu_kernel_ga(int M, int variant);  // activations from global memory, M <= 8
+// MFMA kernels for 16 < M <= 64 (skg_mfma_mt2/3/4.hip: 2, 3, 4 token tiles
+// of 16); nullptr where a combination is not built
+KernelPtr mfma_kernel_mt2(int inner, int row_tiles, int depth);
+KernelPtr mfma_kernel_mt3(int inner, int row_tiles, int depth);
+KernelPtr mfma_kernel_mt4(int inner, int row_tiles, int depth);
+// tokens the VALU kernels (and so the fp32-weight path) take at most
+constexpr int kMaxMValu = 16;
 // the same three tables over fp32 weights (skg_f32w_lo/hi/ga.hip)
 KernelPtr valu_kernel_f32w_lo(int M, int variant);
 KernelPtr valu_kernel_f32w_hi(int M, int variant);

@@ -138,6 +138,13 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth, bool f32w) {
         return nullptr;
     }
     if (f32w) return nullptr;  // matrix-core kernels take bf16 weights only
+    if (M > 16) {  // several token tiles of 16
+        const int mt = (M + 15) / 16;
+        return mt == 2   ? mfma_kernel_mt2(inner, row_tiles, depth)
+               : mt == 3 ? mfma_kernel_mt3(inner, row_tiles, depth)
+               : mt == 4 ? mfma_kernel_mt4(inner, row_tiles, depth)
+                         : nullptr;
+    }
     for (int i = 0; i < kNumMfma; ++i) {
         const MfmaVariant &v = kMfmaVariants[i];
         if (v.G != row_tiles || v.PF != depth) continue;
@@ -168,11 +175,18 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
         static std::set<KernelPtr> done;
         std::lock_guard<std::mutex> lock(mu);
         if (!done.count(fn)) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kMaxLdsBytes);
-            if (e != hipSuccess) return e;
-            done.insert(fn);
+            // resolving the device function loads the kernel's code object,
+            // which the runtime may otherwise defer to the first launch
+            // (raising the limit of a kernel whose code object is not loaded
+            // fails).  Neither step is fatal: if the limit cannot be raised,
+            // the launch below reports whether the LDS it asks for is granted.
+            hipFunction_t dev_fn = nullptr;
+            (void)hipGetFuncBySymbol(&dev_fn, reinterpret_cast<const void *>(fn));
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kMaxLdsBytes) == hipSuccess)
+                done.insert(fn);
+            (void)hipGetLastError();  // neither failure belongs to the launch
         }
     }
     const unsigned grid = (unsigned)g.grid_rb * (unsigned)cfg.split_k;

@@ -126,6 +126,15 @@ WORKLOADS_F32W = {
 }
 
 
+# The middle tier (16 < M <= 64) on the projection shapes: qkv_a-style into
+# the strided bf16 buffer, the wide and the deep projection.
+WORKLOADS_MID = {
+    "mid_m": [dict(M=m, K=k, N=n, out="bf16", ldc=ldc)
+              for (k, n, ldc) in ((7168, 2112, 4096), (1536, 24576, None), (14336, 7168, None))
+              for m in (24, 32, 48, 64)],
+}
+
+
 def all_points():
     """Distinct (M, K, N, out, ldc) points over all workload groups, first-seen order."""
     seen, pts = set(), []

@@ -238,6 +238,17 @@ def skinny_gemm_stream_read(src, sink, nbytes: Optional[int] = None, stream=None
     return sink
 
 
+def skinny_gemm_max_m(K: int, N: int) -> int:
+    """The measured crossover for (K, N): use this library up to this M."""
+    m = ctypes.c_int(0)
+    check(_capi.lib().skinny_gemm_max_m(K, N, ctypes.byref(m)), "skinny_gemm_max_m")
+    return int(m.value)
+
+
+def skinny_gemm_last_hip_error() -> int:
+    return int(_capi.lib().skinny_gemm_last_hip_error())
+
+
 def skinny_gemm_available() -> bool:
     return bool(_capi.lib().skinny_gemm_available())
 

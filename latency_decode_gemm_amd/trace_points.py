@@ -13,7 +13,8 @@ time order; the ones after the i-th marker belong to the i-th point.  A
 call's kernel time is the sum of its dispatches' durations; the table gives
 the median over the timed calls, the weight bandwidth (weight bytes: 2NK,
 or 4NK over fp32 weights) / time and the
-fraction of 8 TB/s, beside the bench's own figures for the point, taken from
+fraction of 8 TB/s, beside the bench's own figures for the point (the
+library GEMM's graph time for the same product among them), taken from
 ``plain.json`` when given: the output of the same command run without the
 profiler, whose event, eager and graph timings the tracing does not inflate.
 """
@@ -73,8 +74,9 @@ def table(trace_path, points_path, plain_path=None):
                   for k, v in points.items()}
     lines = ["| point | config (backend, inner, split, tiles, wn, wk, depth, rb/wg) | "
              "kernel µs (rocprof median) | µs events median | µs/call graph | µs/call hot | "
-             "read ceiling µs | weight GB/s | of 8 TB/s | CPU µs all cores / 1 core |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             "read ceiling µs | weight GB/s | of 8 TB/s | CPU µs all cores / 1 core | "
+             "library GEMM µs/call graph | speed-up vs library |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for name, e in sorted(points.items(), key=lambda kv: kv[1]["trace_order"]):
         us = statistics.median(per[name]["ns"]) / 1000.0
         gbs = e["weight_bytes"] / us / 1e3
@@ -86,7 +88,8 @@ def table(trace_path, points_path, plain_path=None):
         lines.append(f"| {name} | {cfg} | {us:.2f} | {e['kernel_us_events_median']:.2f} | "
                      f"{e['us_per_call_graph']:.2f} | {e['us_per_call_hot_graph']:.2f} | "
                      f"{e['read_ceiling_us_eager']:.2f} | {gbs:.0f} | {gbs / PEAK_GBS:.3f} | "
-                     f"{cpu[0]} / {cpu[1]} |")
+                     f"{cpu[0]} / {cpu[1]} | {e.get('us_per_call_library_graph', '-')} | "
+                     f"{e.get('speedup_vs_library_graph', '-')} |")
     return "\n".join(lines)
 
 

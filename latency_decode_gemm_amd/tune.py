@@ -25,6 +25,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
 TABLE_F32W = os.path.join(PKG, "csrc", "tuned_table_f32w.inc")
+CROSSOVER = os.path.join(PKG, "csrc", "crossover_table.inc")
+CROSSOVER_M = (16, 24, 32, 40, 48, 56, 64)
 
 from latency_decode_gemm_amd._capi import MFMA_VARIANTS, VALU_VARIANTS
 WAVES = [(1, 1), (2, 1), (3, 1), (4, 1), (6, 1), (8, 1), (1, 2), (2, 2), (3, 2), (4, 2),
@@ -241,6 +243,90 @@ def write_table(results, path=TABLE, f32w=False):
         f.write("\n".join(lines) + "\n")
 
 
+def crossover_max_m(times):
+    """{M: (ours_us, library_us)} -> the largest measured M such that this
+    library was faster at every measured M up to it (0 if not even at the
+    smallest)."""
+    best = 0
+    for M in sorted(times):
+        ours, libt = times[M]
+        if ours < libt:
+            best = M
+        else:
+            break
+    return best
+
+
+def write_crossover(entries, path=CROSSOVER):
+    lines = [
+        "// Measured crossover of the tiers per (K, N): the largest M at which the",
+        "// skinny GEMM beat the library GEMM at every measured M up to it, written by",
+        "// `python -m latency_decode_gemm_amd.tune --crossover`.",
+        "// Fields: K, N, max_m   // (M, this library us, library GEMM us) at the measured M",
+        "static const CrossoverEntry kCrossover[] = {",
+    ]
+    for e in entries:
+        detail = " ".join(f"{M}:{o:.1f}/{l:.1f}" for M, (o, l) in sorted(e["times"].items()))
+        lines.append("    {%d, %d, %d},  // %s" % (e["K"], e["N"], e["max_m"], detail))
+    if not entries:
+        lines.append("    {0, 0, 0},  // placeholder, never matches")
+    lines.append("};")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def crossover(torch, lib, skg, inputs, json_path, calls=16):
+    """Times the dispatched configuration and torch.nn.functional.linear
+    (hipBLASLt) on each workload shape for M in CROSSOVER_M, both as HIP
+    graphs of back-to-back calls over rotated weight copies (bf16 out)."""
+    import ctypes
+    F = torch.nn.functional
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    shapes = list(dict.fromkeys((p["K"], p["N"]) for p in inputs.all_points()))
+    entries = []
+    for (K, N) in shapes:
+        bench = Bench(torch, inputs, K, N)
+        times = {}
+        for M in CROSSOVER_M:
+            A = torch.from_numpy(inputs.make_a(M, K, N).view("int16")).cuda().view(torch.bfloat16)
+            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            cfg = skg.skinny_gemm_dispatch(M, K, N)
+            ours = time_config(torch, lib, skg, bench, A, C, M, N, skg.SKG_OUT_BF16, cfg, stream,
+                               calls, reps=2)
+
+            def one():
+                F.linear(A, bench.next())
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    one()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(calls):
+                    one()
+            libt = float("inf")
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                libt = min(libt, e0.elapsed_time(e1) * 1000.0 / calls)
+            del g
+            times[M] = (ours, libt)
+            print(f"K={K:5d} N={N:5d} M={M:2d}: this library {ours:8.2f} us, library GEMM "
+                  f"{libt:8.2f} us", flush=True)
+        entries.append({"K": K, "N": N, "max_m": crossover_max_m(times), "times": times})
+        del bench
+        torch.cuda.empty_cache()
+    with open(json_path, "w") as f:
+        json.dump([dict(e, times={str(m): t for m, t in e["times"].items()}) for e in entries],
+                  f, indent=1)
+    write_crossover(entries)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--points", default="all", help="all, a workload name, or M,K,N;M,K,N")
@@ -251,6 +337,10 @@ def main():
     ap.add_argument("--top", type=int, default=6)
     ap.add_argument("--weights", choices=("bf16", "f32"), default="bf16",
                     help="f32: tune the fp32-weight entry points over their workload")
+    ap.add_argument("--crossover", default=None, metavar="JSON",
+                    help="measure this library (dispatched configuration) against the "
+                         "library GEMM at M = 16 .. 64 on the workload shapes, write the "
+                         "results to JSON and the crossover table to csrc/crossover_table.inc")
     args = ap.parse_args()
     f32w = args.weights == "f32"
     table_path = TABLE_F32W if f32w else TABLE
@@ -265,14 +355,19 @@ def main():
     from latency_decode_gemm_amd import _capi, inputs
 
     lib = _capi.lib()
-    universe = inputs.WORKLOADS_F32W["router_f32w"] if f32w else inputs.all_points()
+    universe = (inputs.WORKLOADS_F32W["router_f32w"] if f32w else
+                inputs.all_points() + inputs.WORKLOADS_MID["mid_m"])
     check = skg.skinny_gemm_f32w_check_config if f32w else skg.skinny_gemm_check_config
     dispatch = skg.skinny_gemm_f32w_dispatch if f32w else skg.skinny_gemm_dispatch
     run_cfg = skg.skinny_gemm_f32w_with_config if f32w else skg.skinny_gemm_bf16_with_config
+    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_MID)
+    if args.crossover:
+        crossover(torch, lib, skg, inputs, args.crossover)
+        return
     if args.points == "all":
         pts = universe
-    elif args.points in inputs.WORKLOADS:
-        pts = inputs.WORKLOADS[args.points]
+    elif args.points in groups:
+        pts = groups[args.points]
     else:
         want = [tuple(int(x) for x in s.split(",")) for s in args.points.split(";")]
         pts = [p for p in universe if (p["M"], p["K"], p["N"]) in want]
@@ -299,7 +394,8 @@ def main():
             C = torch.zeros((M, ldc), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                             device="cuda")
             inner_set = ([0, 3] if M < 2 or f32w else [0, 3, 1, 2, 4, 5] if M <= 8 else
-                         [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0])
+                         [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0] if M <= 16 else
+                         [1, 2, 4, 5])
             cands = structures(skg, M, K, N, inner_set, check)
             timed = {}
             print(f"M={M} K={K} N={N}: {len(cands)} stage-1 candidates", file=sys.stderr,

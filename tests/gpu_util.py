@@ -87,3 +87,20 @@ def assess_f32w(C, A_bits, W, K, C_ref=None) -> dict:
     wn = acceptance.row_norms(np.asarray(W, dtype=np.float64), K)
     odt = "bf16" if C.dtype == torch.bfloat16 else "f32"
     return acceptance.assess(to_f64(C), C_ref, an, wn, odt)
+
+
+def assess_sampled(C, A_bits, B_bits, K, ncols=96, seed=0) -> dict:
+    """The acceptance measures on every row and a sample of columns, the
+    oracle computing each sampled output on its own (full-size shapes)."""
+    torch = torch_cuda()
+    N = C.shape[1]
+    M = C.shape[0]
+    rng = np.random.default_rng(seed)
+    ns = np.sort(rng.choice(N, size=min(ncols, N), replace=False))
+    ms = np.repeat(np.arange(M), ns.size)
+    nn = np.tile(ns, M)
+    ref = oracle.gemm_points(A_bits, B_bits, K, ms, nn).reshape(M, ns.size)
+    an = acceptance.row_norms(oracle.bf16_decode(A_bits), K)
+    bn = acceptance.row_norms(oracle.bf16_decode(B_bits[ns]), K)
+    odt = "bf16" if C.dtype == torch.bfloat16 else "f32"
+    return acceptance.assess(to_f64(C)[:, ns], ref, an, bn, odt)

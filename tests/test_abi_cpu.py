@@ -58,7 +58,7 @@ def test_dispatch_is_pure_and_deterministic():
 
 
 def test_dispatch_valid_on_a_shape_grid():
-    for M in range(1, 17):
+    for M in list(range(1, 18)) + [24, 31, 32, 33, 40, 48, 56, 63, 64]:
         for K in (1, 7, 8, 9, 64, 100, 1000, 1536, 2048, 2880, 4096, 7168, 14336, 20000):
             for N in (1, 3, 16, 128, 129, 2112, 24576):
                 cfg = skg.skinny_gemm_dispatch(M, K, N)
@@ -72,7 +72,9 @@ def test_dispatch_valid_on_a_shape_grid():
 def test_dispatch_rejects():
     lib = _capi.lib()
     cfg = _capi.SkgConfig()
-    assert lib.skinny_gemm_dispatch(17, 7168, 256, ctypes.byref(cfg)) == skg.SKG_ERR_UNSUPPORTED
+    assert lib.skinny_gemm_dispatch(65, 7168, 256, ctypes.byref(cfg)) == skg.SKG_ERR_UNSUPPORTED
+    assert lib.skinny_gemm_f32w_dispatch(17, 7168, 256, ctypes.byref(cfg)) == \
+        skg.SKG_ERR_UNSUPPORTED
     assert lib.skinny_gemm_dispatch(0, 7168, 256, ctypes.byref(cfg)) == skg.SKG_ERR_INVALID_ARG
     assert lib.skinny_gemm_dispatch(1, -1, 256, ctypes.byref(cfg)) == skg.SKG_ERR_INVALID_ARG
     assert lib.skinny_gemm_dispatch(1, 7168, 256, None) == skg.SKG_ERR_INVALID_ARG
@@ -248,7 +250,7 @@ def _call(A=FAKE, B=FAKE, C=FAKE, M=4, N=256, K=7168, lda=7168, ldb=7168, ldc=25
     (dict(M=-1), skg.SKG_ERR_INVALID_ARG),
     (dict(N=-1), skg.SKG_ERR_INVALID_ARG),
     (dict(K=-1), skg.SKG_ERR_INVALID_ARG),
-    (dict(M=17), skg.SKG_ERR_UNSUPPORTED),
+    (dict(M=65), skg.SKG_ERR_UNSUPPORTED),
     (dict(odt=2), skg.SKG_ERR_INVALID_ARG),
     (dict(lda=7160), skg.SKG_ERR_INVALID_ARG),
     (dict(ldb=100), skg.SKG_ERR_INVALID_ARG),
@@ -371,3 +373,74 @@ def test_f32w_spilling_variants_are_not_built():
     assert skg.skinny_gemm_f32w_check_config(7, 1024, 512, ga)
     assert not skg.skinny_gemm_f32w_check_config(8, 1024, 512, ga)
     assert skg.skinny_gemm_check_config(8, 1024, 512, ga)
+
+
+# --- the middle tier (16 < M <= 64) ---------------------------------------------
+
+def test_mid_tier_rules():
+    """Above 16 tokens only the matrix-core kinds run, each token tile of 16
+    costing its own activation tile (LDS-staged fragments or a transpose /
+    ring tile); combinations that would spill are not built."""
+    mk = _capi.SkgConfig.make
+    F, GA = skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
+    RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
+    for M in (17, 32, 33, 64):
+        assert not skg.skinny_gemm_check_config(M, 7168, 2112, mk(
+            inner=skg.SKG_INNER_VALU, row_tiles=1, depth=4, waves_n=2, waves_k=2))
+        assert skg.skinny_gemm_check_config(M, 7168, 2112, mk(
+            inner=RG, row_tiles=1, depth=2, waves_n=2, waves_k=1))
+        # staged fragments of a 1024-wide K slice: 32 KB per token tile
+        assert skg.skinny_gemm_check_config(M, 7168, 2112, mk(
+            inner=F, split_k=7, row_tiles=1, depth=4, waves_n=1, waves_k=2))
+    # LDS ring with 4 row tiles spills above one token tile: not built
+    ring4 = mk(inner=RG, row_tiles=4, depth=1, waves_n=1, waves_k=1)
+    assert skg.skinny_gemm_check_config(16, 7168, 2112, ring4)
+    assert not skg.skinny_gemm_check_config(17, 7168, 2112, ring4)
+    # 2 row tiles x 3 token tiles is built, x 4 is not
+    ring2 = mk(inner=RG, row_tiles=2, depth=2, waves_n=1, waves_k=1)
+    assert skg.skinny_gemm_check_config(48, 7168, 2112, ring2)
+    assert not skg.skinny_gemm_check_config(49, 7168, 2112, ring2)
+    # register ring of activations: 4 x depth x loads + 4 x accumulator tiles <= 176
+    assert skg.skinny_gemm_check_config(64, 7168, 2112, mk(inner=GA, row_tiles=2, depth=1,
+                                                          waves_n=1, waves_k=1))
+    assert not skg.skinny_gemm_check_config(64, 7168, 2112, mk(inner=GA, row_tiles=4, depth=1,
+                                                              waves_n=1, waves_k=1))
+    # staged activations: K x 16 tokens x 2 B per token tile; 64 x 2880 fits
+    # (368 KB does not: K = 7168 needs a split)
+    st = mk(inner=F, row_tiles=1, depth=2, waves_n=1, waves_k=1)
+    assert skg.skinny_gemm_check_config(64, 1024, 2112, st)
+    assert not skg.skinny_gemm_check_config(64, 7168, 2112, st)
+    # the split-K workspace holds M rows of partials per block
+    sk = mk(inner=GA, split_k=4, row_tiles=1, depth=2, waves_n=1, waves_k=1)
+    nrb = -(-2112 // 16)
+    assert skg.skinny_gemm_workspace_bytes(48, 7168, 2112, sk) == nrb * 4 * 48 * 16 * 4 + nrb * 4
+
+
+def test_mid_tier_dispatch_and_crossover_defaults():
+    for (K, N) in ((7168, 2112), (1536, 24576), (14336, 7168), (100, 7), (2880, 128)):
+        for M in (17, 24, 32, 48, 64):
+            cfg = skg.skinny_gemm_dispatch(M, K, N)
+            assert cfg.inner in (skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA,
+                                 skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA)
+            assert skg.skinny_gemm_check_config(M, K, N, cfg)
+    # an unmeasured shape: the skinny tier's own range
+    assert skg.skinny_gemm_max_m(1000, 77) == skg.SKG_MAX_M_VALU
+    lib = _capi.lib()
+    m = ctypes.c_int(0)
+    assert lib.skinny_gemm_max_m(7168, 0, ctypes.byref(m)) == skg.SKG_ERR_INVALID_ARG
+    assert lib.skinny_gemm_max_m(7168, 256, None) == skg.SKG_ERR_INVALID_ARG
+    for (K, N) in ((7168, 2112), (1536, 24576), (14336, 7168)):
+        assert 1 <= skg.skinny_gemm_max_m(K, N) <= skg.SKG_MAX_M
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """Loading the library through the binding leaves one HIP runtime in the
+    process (torch's), even when nothing imported torch before."""
+    import subprocess
+    import sys
+    code = ("from latency_decode_gemm_amd import _capi; _capi.lib(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip().splitlines()[-1]
+    libs = eval(out)
+    assert len(libs) == 1, libs

@@ -189,10 +189,14 @@ def test_large_shapes(shape, cfg):
 
 def test_error_returns():
     torch = gu.torch_cuda()
-    A17 = torch.zeros((17, 64), dtype=torch.bfloat16, device="cuda")
+    A65 = torch.zeros((65, 64), dtype=torch.bfloat16, device="cuda")
     B = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(skg.SkinnyGemmError) as e:
-        skg.skinny_gemm_bf16(A17, B)
+        skg.skinny_gemm_bf16(A65, B)
+    assert e.value.status == skg.SKG_ERR_UNSUPPORTED
+    # over fp32 weights the VALU kernels take at most 16 tokens
+    with pytest.raises(skg.SkinnyGemmError) as e:
+        skg.skinny_gemm_f32w(A65[:17], torch.zeros((8, 64), dtype=torch.float32, device="cuda"))
     assert e.value.status == skg.SKG_ERR_UNSUPPORTED
     # A offset by one element: not 16-byte aligned
     base = torch.zeros((4, 72), dtype=torch.bfloat16, device="cuda")

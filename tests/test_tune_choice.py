@@ -29,3 +29,10 @@ def test_input_timings_untouched():
     timed = {ONE: 11.8, TWO: 11.56}
     tune.choose(timed, lambda c: True)
     assert timed[TWO] == 11.56
+
+
+def test_crossover_is_the_last_m_of_the_winning_prefix():
+    from latency_decode_gemm_amd.tune import crossover_max_m
+    assert crossover_max_m({16: (1, 2), 24: (1, 2), 32: (3, 2), 40: (1, 2)}) == 24
+    assert crossover_max_m({16: (3, 2), 24: (1, 2)}) == 0
+    assert crossover_max_m({16: (1, 2), 64: (1, 2)}) == 64
