@@ -333,7 +333,10 @@ bool config_ok(int M, int K, int N, const skg_config &cfg, bool f32w) {
     return !f32w || variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, true, M);
 }
 
-// The tuned entry for (M, K, N), else the default rule; pure.
+// The tuned entry for (M, K, N); else, for the same (K, N), the entry of the
+// smallest tuned M above M whose configuration can run M (the table is keyed
+// by (K, N), then M, and a configuration measured for a few more tokens is
+// closer to the best than the default rule); else the default rule.  Pure.
 int dispatch_impl(int M, int K, int N, bool f32w, skg_config *out) {
     if (!out) return SKG_ERR_INVALID_ARG;
     const int max_m = f32w ? kMaxMValu : SKG_MAX_M;
@@ -341,14 +344,17 @@ int dispatch_impl(int M, int K, int N, bool f32w, skg_config *out) {
     if (M > max_m) return SKG_ERR_UNSUPPORTED;
     const TableEntry *table = f32w ? kTunedTableF32w : kTunedTable;
     const int n = f32w ? kNumTableF32w : kNumTable;
+    const TableEntry *above = nullptr;
     for (int i = 0; i < n; ++i) {
         const TableEntry &e = table[i];
-        if (e.M == M && e.K == K && e.N == N && config_ok(M, K, N, e.cfg, f32w)) {
+        if (e.K != K || e.N != N || e.M < M || !config_ok(M, K, N, e.cfg, f32w)) continue;
+        if (e.M == M) {
             *out = e.cfg;
             return SKG_OK;
         }
+        if (!above || e.M < above->M) above = &e;
     }
-    *out = default_config(M, K, N, f32w);
+    *out = above ? above->cfg : default_config(M, K, N, f32w);
     return SKG_OK;
 }
 

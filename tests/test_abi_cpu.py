@@ -444,3 +444,29 @@ def test_binding_shares_torchs_hip_runtime():
                          check=True).stdout.strip().splitlines()[-1]
     libs = eval(out)
     assert len(libs) == 1, libs
+
+
+def test_untuned_m_takes_the_next_tuned_m_of_its_shape():
+    """An M the table does not list takes the configuration tuned for the
+    smallest listed M above it on the same (K, N), when that can run M."""
+    import re
+    table = open(os.path.join(ROOT, "latency_decode_gemm_amd", "csrc", "tuned_table.inc")).read()
+    rows = [tuple(int(v) for v in m.groups()) for m in
+            re.finditer(r"\{(\d+), (\d+), (\d+), \{([-\d]+), ([-\d]+), ([-\d]+), ([-\d]+), "
+                        r"([-\d]+), ([-\d]+), ([-\d]+), ([-\d]+)\}\}", table)]
+    tuned = {}
+    for r in rows:
+        tuned.setdefault((r[1], r[2]), {})[r[0]] = _capi.SkgConfig(*r[3:])
+    checked = 0
+    for (K, N), by_m in tuned.items():
+        for M in range(1, 65):
+            got = skg.skinny_gemm_dispatch(M, K, N)
+            if M in by_m:
+                assert got == by_m[M], (M, K, N)
+                continue
+            above = [m for m in sorted(by_m) if m > M
+                     and skg.skinny_gemm_check_config(M, K, N, by_m[m])]
+            if above:
+                assert got == by_m[above[0]], (M, K, N)
+                checked += 1
+    assert checked > 50
