@@ -53,6 +53,7 @@ PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30  # footprint between two uses of one weight copy
 DEFAULT_WORKLOAD = "wide_deep"
+GRAPH_STEPS = 4  # steps per captured graph (each weight copy recurs every 4 steps)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # what the counters depend on: the kernels' code (the configuration they were
 # taken with is stored beside them and compared separately)
@@ -83,6 +84,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default=None,
                     help="profile helper: run only the point 'M,K,N' (no JSON checks)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph (GRAPH_STEPS steps "
+                         "captured with rotating weight copies): ms_per_step_graph")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -433,7 +437,8 @@ def main():
         print("bench.py: libskinny_gemm.so has no gfx950 device/code to run", file=sys.stderr)
         sys.exit(1)
 
-    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_F32W, **inputs.WORKLOADS_MID)
+    groups = dict(inputs.WORKLOADS, **inputs.WORKLOADS_F32W, **inputs.WORKLOADS_MID,
+                  **inputs.WORKLOADS_CHAIN)
     workload = groups[args.workload]
     if args.only:
         M, K, N = (int(x) for x in args.only.split(","))
@@ -485,6 +490,30 @@ def main():
     dom_us = float(np.mean([a.elapsed_ms(b) for a, b in zip(ev_s, ev_e)])) * 1000.0
     achieved = dom.alg_bytes / (dom_us * 1e-6) / 1e9
 
+    graph_ms = None
+    if args.graph:
+        # the same step captured (GRAPH_STEPS steps, rotating copies) and
+        # replayed: no host launch work between the kernels of the chain
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(GRAPH_STEPS):
+                for pt in pts:
+                    call(lib, pt, next_copy(pt), h)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // GRAPH_STEPS)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * GRAPH_STEPS)
+        del g
+
     # results are still right after the timed loop (sampled oracle check)
     bad = []
     if not args.only:
@@ -531,6 +560,7 @@ def main():
                    "parallelism": "single GPU", "weight_copies_rotated": True,
                    "host_wall_s": round(wall, 3)},
         "us_per_call_eager": per_point,
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

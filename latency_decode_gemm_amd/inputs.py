@@ -135,6 +135,18 @@ WORKLOADS_MID = {
 }
 
 
+# One decode layer's chain of GEMMs at a small batch (the analogue of the
+# launch-latency hiding the pages pursue with programmatic dependent launch):
+# the MoE router over fp32 weights, the qkv_a-style projection into its
+# strided buffer, the wide and the deep projection, back to back.
+WORKLOADS_CHAIN = {
+    "decode_chain": [dict(M=4, K=7168, N=256, out="f32", ldc=None, w="f32"),
+                     dict(M=4, K=7168, N=2112, out="bf16", ldc=4096),
+                     dict(M=4, K=1536, N=24576, out="bf16", ldc=None),
+                     dict(M=4, K=14336, N=7168, out="bf16", ldc=None)],
+}
+
+
 def all_points():
     """Distinct (M, K, N, out, ldc) points over all workload groups, first-seen order."""
     seen, pts = set(), []
