@@ -132,3 +132,26 @@ def test_mid_repeated_calls_identical():
         torch.cuda.synchronize()
         for o in outs:
             assert np.array_equal(gu.bits_of(o), ref), (M, K, N)
+
+
+@pytest.mark.parametrize("M", [17, 31, 48, 64])
+def test_mid_edges(M):
+    """K = 0 (zeros), K < 8 (one thread per output), K = 8, 9 (one window and
+    a ragged one), N = 1 and 3, into a strided bf16 buffer whose padding
+    columns stay untouched."""
+    torch = gu.torch_cuda()
+    for K in (0, 1, 7, 8, 9, 130):
+        for N in (1, 3, 37):
+            ld = max(8, gu.round8(K))
+            A_bits = inputs.make_a(M, K, N, lda=ld)
+            B_bits = inputs.make_b(K, N, ldb=ld)
+            A, B = gu.operands(A_bits, B_bits, K)
+            buf = torch.full((M, N + 5), float("nan"), dtype=torch.bfloat16, device="cuda")
+            skg.skinny_gemm_bf16(A, B, out=buf[:, :N])
+            torch.cuda.synchronize()
+            if K == 0:
+                assert np.all(gu.to_f64(buf[:, :N]) == 0.0), (M, K, N)
+            else:
+                r = gu.assess(buf[:, :N], A_bits, B_bits, K)
+                assert r["ok"], (M, K, N, r)
+            assert np.isnan(gu.to_f64(buf[:, N:])).all(), (M, K, N)
