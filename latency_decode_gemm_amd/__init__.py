@@ -1,4 +1,5 @@
-"""MI355X (gfx950) small-M bf16 "skinny" GEMM: C = A . B^T for M <= 16.
+"""MI355X (gfx950) small-M bf16 "skinny" GEMM: C = A . B^T for M <= 16, with a
+middle tier to M <= 64 and a router GEMM over fp32 weights.
 
 The computation runs in ``libskinny_gemm.so`` (hand-written HIP kernels behind
 the C ABI in ``include/skinny_gemm.h``); this package only marshals PyTorch

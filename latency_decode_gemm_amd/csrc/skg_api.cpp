@@ -11,7 +11,8 @@
 // as get_warmup_keys does on that page.
 //
 // Eligibility mirrors the router gate of the same page (item 4 and the
-// review section 评论区精华): M <= 16, bf16 operands, 16-byte aligned 128-bit
+// review section 评论区精华): M <= 16 (here 64 with the middle tier of the
+// PR #48597 page, section 实现拆解 item 3), bf16 operands, 16-byte aligned 128-bit
 // loads; anything else is rejected with a status code so the caller can fall
 // back to another GEMM.
 #include <hip/hip_runtime.h>

@@ -1,4 +1,5 @@
-// skg_device.h -- gfx950 kernels for C[M,N] = A[M,K] . B[N,K]^T, M <= 16.
+// skg_device.h -- gfx950 kernels for C[M,N] = A[M,K] . B[N,K]^T, M <= 16 (the
+// matrix-core kernels: M <= 64 with up to four token tiles of 16).
 //
 // What is computed follows the PR #42562 page ("Add generic cuteDSL LL BF16
 // router (GEMM)"): section 实现拆解 item 1 and the _ll_bf16_dotprod.py excerpt

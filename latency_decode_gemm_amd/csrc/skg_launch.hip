@@ -104,7 +104,7 @@ struct MfmaVariant {
     int G, PF;
     KernelPtr lds_a;  // activations staged in LDS
     KernelPtr ga2;    // activations loaded from global memory, M <= 8
-    KernelPtr ga4;    // activations loaded from global memory, M <= 16
+    KernelPtr ga4;    // activations loaded from global memory, M <= 16 (one token tile)
     KernelPtr ring_lds_a, ring_ga2, ring_ga4;  // the same with the LDS ring
 };
 #define SKG_MFMA(G, PF)                                                                 \

@@ -74,7 +74,7 @@ def _marshal(A, B, out, out_dtype, f32w=False):
 
 
 def skinny_gemm_bf16(A, B, out=None, out_dtype=None, stream=None):
-    """C = A . B^T (A [M, K], B [N, K], bf16; M <= 16) into ``out`` (fp32 or
+    """C = A . B^T (A [M, K], B [N, K], bf16; M <= 64) into ``out`` (fp32 or
     bf16, may be a strided view).  Returns ``out``."""
     M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, out_dtype)
     st = _capi.lib().skinny_gemm_bf16(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,

@@ -442,7 +442,8 @@ def test_binding_shares_torchs_hip_runtime():
             "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.strip().splitlines()[-1]
-    libs = eval(out)
+    import ast
+    libs = ast.literal_eval(out)
     assert len(libs) == 1, libs
 
 
