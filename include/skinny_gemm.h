@@ -42,6 +42,9 @@
  *   - Thread safety: all entry points may be called from several host
  *     threads.  Calls on different streams use different workspaces; calls
  *     on one stream are ordered by the stream.
+ *   - Logging: with SKINNY_GEMM_LOG=1 in the environment, the first GEMM call
+ *     of each (weight type, M, K, N) prints the chosen configuration to
+ *     stderr.  No environment variable changes the dispatch.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
@@ -142,7 +145,8 @@ typedef struct skg_config {
  *   B: device bf16 [N, ldb], 16-byte aligned, ldb % 8 == 0, ldb >= K.
  *   C: device [M, ldc] of fp32 (out_dtype SKG_OUT_F32, 4-byte aligned) or
  *      bf16 (SKG_OUT_BF16, 2-byte aligned, round to nearest even), ldc >= N.
- *   0 <= M <= 64 (M > 64 -> SKG_ERR_UNSUPPORTED), N >= 0, K >= 0.
+ *   0 <= M <= 64 (M > 64 -> SKG_ERR_UNSUPPORTED), 0 <= N <= 2^30,
+ *   0 <= K <= 2^28 (larger: SKG_ERR_INVALID_ARG).
  *   M == 0 or N == 0: nothing is written, SKG_OK.  K == 0: C gets zeros.
  * The result for a given (M, K, N) and inputs is bit-identical from call to
  * call (fixed summation order; no floating-point atomics).
@@ -170,7 +174,10 @@ int skinny_gemm_bf16_with_config(const void *A, const void *B, void *C, int M,
 
 /* The configuration used for (M, K, N).  Pure host function: no GPU access,
  * deterministic, the same answer on every call.  M must be in 1..64,
- * K >= 0, N >= 1; otherwise SKG_ERR_INVALID_ARG / SKG_ERR_UNSUPPORTED. */
+ * K >= 0, N >= 1; otherwise SKG_ERR_INVALID_ARG / SKG_ERR_UNSUPPORTED.
+ * SKG_ERR_UNSUPPORTED also when no configuration can run the shape (only far
+ * outside the decode range).  The returned configuration always passes
+ * skinny_gemm_check_config. */
 int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
 
 /* Whether cfg can run (M, K, N): SKG_OK or SKG_ERR_INVALID_ARG.  Pure host. */

@@ -18,10 +18,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <set>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -49,8 +52,9 @@ constexpr int kNumTable = sizeof(kTunedTable) / sizeof(kTunedTable[0]);
 constexpr int kNumTableF32w = sizeof(kTunedTableF32w) / sizeof(kTunedTableF32w[0]);
 
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
-int round_up(int a, int b) { return ceil_div(a, b) * b; }
+// (in 64 bits, so that sizes near the int range cannot overflow)
+int ceil_div(int a, int b) { return (int)(((int64_t)a + b - 1) / b); }
+int round_up(int a, int b) { return (int)((((int64_t)a + b - 1) / b) * b); }
 
 bool config_equal(const skg_config &a, const skg_config &b) {
     return a.backend == b.backend && a.inner == b.inner && a.split_k == b.split_k &&
@@ -82,11 +86,17 @@ skg_config default_config(int M, int K, int N, bool f32w = false) {
     while (c.inner == SKG_INNER_VALU && S < 16 &&
            (int64_t)M * ceil_div(nck, S) * kChunk * 2 > 64 * 1024)
         S *= 2;
-    while (S < 16 && num_rb * S < 256 && ceil_div(nck, 2 * S) >= 2 * step * c.waves_k) S *= 2;
+    while (S < 16 && (int64_t)num_rb * S < 256 && ceil_div(nck, 2 * S) >= 2 * step * c.waves_k)
+        S *= 2;
     c.split_k = S;
     c.backend = (S > 1) ? SKG_BACKEND_SPLITK : SKG_BACKEND_DOT;
-    c.rb_per_wg = std::max(1, (num_rb * S) / 512);
+    c.rb_per_wg = (int)std::max<int64_t>(1, ((int64_t)num_rb * S) / 512);
     Geometry g;
+    auto valid = [&](const skg_config &x) {
+        return make_geometry(M, K, N, x, &g) &&
+               (!f32w || variant_exists(x.inner, x.row_tiles, x.depth, true, M));
+    };
+    const skg_config first = c;
     // back off until the geometry is valid (an empty last split, LDS size)
     while (c.split_k > 1 && !make_geometry(M, K, N, c, &g)) {
         c.split_k /= 2;
@@ -95,7 +105,41 @@ skg_config default_config(int M, int K, int N, bool f32w = false) {
     while (!make_geometry(M, K, N, c, &g) && c.waves_k > 1) c.waves_k /= 2;
     // the stash holds rb_per_wg row blocks: more workgroups if it does not fit
     while (!make_geometry(M, K, N, c, &g) && c.rb_per_wg > 1) c.rb_per_wg /= 2;
-    return c;
+    if (valid(c)) return c;
+    // Very long rows or very many of them: keep the split that makes the
+    // staged activations fit and give up row blocks per workgroup first,
+    // then split K further (one K-wave, one row block as the last resort),
+    // then load the activations from global memory instead of staging them.
+    skg_config t = first;
+    for (t.rb_per_wg = first.rb_per_wg; t.rb_per_wg >= 1; t.rb_per_wg /= 2)
+        if (valid(t)) return t;
+    for (int S = std::max(2, first.split_k); S <= 4096; S *= 2)
+        for (int wk : {first.waves_k, 1})
+            for (int rpw : {first.rb_per_wg, 1}) {
+                t = first;
+                t.split_k = S;
+                t.backend = SKG_BACKEND_SPLITK;
+                t.waves_k = wk;
+                t.rb_per_wg = rpw;
+                if (valid(t)) return t;
+            }
+    t = first;
+    t.split_k = 1;
+    t.backend = SKG_BACKEND_DOT;
+    t.waves_n = 1;
+    t.waves_k = 1;
+    t.rb_per_wg = 1;
+    if (!f32w) {
+        t.inner = SKG_INNER_MFMA_GA;
+        t.row_tiles = 1;
+        t.depth = 2;
+    } else {
+        t.inner = SKG_INNER_VALU_GA;
+        t.row_tiles = 1;
+        t.depth = 4;
+    }
+    if (valid(t)) return t;
+    return c;  // nothing runs this shape: the caller reports it
 }
 
 // The HIP error behind this thread's last SKG_ERR_HIP (hipSuccess if none).
@@ -238,12 +282,15 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
 
 bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (M < 1 || M > SKG_MAX_M || K < 0 || N < 1) return false;
+    if (K > kMaxK || N > kMaxN) return false;
     if (cfg.backend == SKG_BACKEND_DOT) {
         if (cfg.split_k != 1) return false;
     } else if (cfg.backend == SKG_BACKEND_EVEN) {
         // the 256 x rb_per_wg workgroups are num_rb row blocks x split_k slices
         if (cfg.split_k < 1 || cfg.split_k > 64) return false;
-        if (cfg.rb_per_wg < 1 || (kEvenUnit * cfg.rb_per_wg) % cfg.split_k != 0) return false;
+        if (cfg.rb_per_wg < 1 || cfg.rb_per_wg > 64 ||
+            (kEvenUnit * cfg.rb_per_wg) % cfg.split_k != 0)
+            return false;
     } else if (cfg.backend == SKG_BACKEND_SPLITK || cfg.backend == SKG_BACKEND_SPLITK_2PASS) {
         if (cfg.split_k < 2 || cfg.split_k > 4096) return false;
     } else {
@@ -258,7 +305,9 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (valu && M > kMaxMValu) return false;
     if (!variant_exists(cfg.inner, cfg.row_tiles, cfg.depth, false, M)) return false;
     const int mt = (M + 15) / 16;  // MFMA token tiles of 16
-    if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n * cfg.waves_k > kMaxWaves) return false;
+    if (cfg.waves_n < 1 || cfg.waves_k < 1 || cfg.waves_n > kMaxWaves ||
+        cfg.waves_k > kMaxWaves || cfg.waves_n * cfg.waves_k > kMaxWaves)
+        return false;
     if (cfg.rb_per_wg < 1) return false;
     Geometry r;
     r.step = kValuStep;
@@ -291,6 +340,7 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
         a_bytes = (size_t)M * r.lds_stride * 2;
     else if (lds_frag)
         a_bytes = (size_t)(r.wg_chunks / 4) * 64 * 16 * mt;
+    if (a_bytes > (size_t)kMaxLdsBytes) return false;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
     // MFMA: one transpose tile per 16-row tile of B per wave, plus one per
     // token tile for A (GA) (the LDS ring: depth slots of those tiles)
@@ -355,8 +405,34 @@ int dispatch_impl(int M, int K, int N, bool f32w, skg_config *out) {
         }
         if (!above || e.M < above->M) above = &e;
     }
-    *out = above ? above->cfg : default_config(M, K, N, f32w);
-    return SKG_OK;
+    if (above) {
+        *out = above->cfg;
+        return SKG_OK;
+    }
+    *out = default_config(M, K, N, f32w);
+    // (only shapes far outside the decode range, e.g. fp32 weights with
+    // millions of columns and more than 8 tokens, have no configuration)
+    return config_ok(M, K, N, *out, f32w) ? SKG_OK : SKG_ERR_UNSUPPORTED;
+}
+
+// With SKINNY_GEMM_LOG=1 in the environment, the first call of each
+// (weights, M, K, N) prints the configuration dispatch chose to stderr.  It
+// only reports: nothing in the environment changes what dispatch returns.
+void log_choice(bool f32w, int M, int K, int N, const skg_config &c) {
+    static const bool on = [] {
+        const char *v = std::getenv("SKINNY_GEMM_LOG");
+        return v && v[0] == '1';
+    }();
+    if (!on) return;
+    static std::mutex mu;
+    static std::set<std::tuple<bool, int, int, int>> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!seen.insert(std::make_tuple(f32w, M, K, N)).second) return;
+    std::fprintf(stderr,
+                 "skinny_gemm: %s M=%d K=%d N=%d -> backend %d inner %d split_k %d row_tiles %d "
+                 "waves_n %d waves_k %d depth %d rb_per_wg %d\n",
+                 f32w ? "fp32 weights" : "bf16", M, K, N, c.backend, c.inner, c.split_k,
+                 c.row_tiles, c.waves_n, c.waves_k, c.depth, c.rb_per_wg);
 }
 
 // Warm-up keys and warm-up over bf16 (f32w false) or fp32 weights.
@@ -496,6 +572,7 @@ int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
     skg_config cfg;
     const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
     if (ds != SKG_OK) return ds;
+    log_choice(false, M, K, N, cfg);
     return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg);
 }
 
@@ -507,6 +584,7 @@ int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, 
     skg_config cfg;
     const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
     if (ds != SKG_OK) return ds;
+    log_choice(false, M, K, N, cfg);
     return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg, start_event, stop_event);
 }
 
@@ -550,6 +628,7 @@ int skinny_gemm_f32w_timed(const void *A, const void *W, void *C, int M, int N, 
     skg_config cfg;
     const int ds = dispatch_impl(M, K, N, true, &cfg);
     if (ds != SKG_OK) return ds;
+    log_choice(true, M, K, N, cfg);
     return run(A, W, C, M, N, K, lda, ldw, ldc, out_dtype, stream, cfg, start_event, stop_event,
                true);
 }

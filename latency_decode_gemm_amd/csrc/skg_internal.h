@@ -21,6 +21,9 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
 // SKG_BACKEND_EVEN: workgroups per rb_per_wg (the CU count of MI355X)
 constexpr int kEvenUnit = 256;
+// Largest K and N a configuration takes (the launch geometry stays in int).
+constexpr int kMaxK = 1 << 28;
+constexpr int kMaxN = 1 << 30;
 
 // Everything a kernel needs, passed by value.
 struct KParams {

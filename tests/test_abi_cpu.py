@@ -471,3 +471,23 @@ def test_untuned_m_takes_the_next_tuned_m_of_its_shape():
                 assert got == by_m[above[0]], (M, K, N)
                 checked += 1
     assert checked > 50
+
+
+def test_log_env_prints_the_choice_once_per_shape():
+    """SKINNY_GEMM_LOG=1: the entry point reports dispatch's choice once per
+    shape (before any device work; on a machine without a GPU the call then
+    fails with a status, which is all this checks besides the log)."""
+    import subprocess
+    import sys
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("needs a machine without a GPU: the call passes placeholder pointers")
+    code = ("from latency_decode_gemm_amd import _capi; lib = _capi.lib(); "
+            "[lib.skinny_gemm_bf16(0x100000, 0x100000, 0x100000, 4, 256, 7168, 7168, 7168, 256, 0,"
+            " None) for _ in range(3)]")
+    env = dict(os.environ, SKINNY_GEMM_LOG="1", HIP_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       env=env, timeout=120)
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("skinny_gemm: bf16 M=4 K=7168")]
+    cfg = skg.skinny_gemm_dispatch(4, 7168, 256)
+    assert len(lines) == 1, r.stderr
+    assert f"backend {cfg.backend} inner {cfg.inner} split_k {cfg.split_k}" in lines[0]
