@@ -22,7 +22,7 @@ Prints ONE JSON line:
 (skinny_gemm_f32w; weight bytes 4*N*K) the same way, ``--workload mid_m`` the
 middle tier (16 < M <= 64) on the projection shapes.
 ``--points-out FILE`` also writes, for every one of the 29 workload points,
-the 12 fp32-weight router points and the 12 middle-tier points, the library
+the 12 fp32-weight router points and the 24 middle-tier points, the library
 GEMM's time for the same
 product (torch.nn.functional.linear: hipBLASLt), and
 the kernel time per call (median of 200 dispatch-recorded event pairs), the
@@ -318,7 +318,7 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
     kernel trace of this run can be attributed to points by order."""
     h = stream.cuda_stream
     spec = (inputs.all_points() + inputs.WORKLOADS_F32W["router_f32w"] +
-            inputs.WORKLOADS_MID["mid_m"])
+            inputs.WORKLOADS_MID["mid_m"] + inputs.WORKLOADS_MID["mid_router"])
 
     def key_of(p):
         return (p["K"], p["N"], p.get("w") == "f32")

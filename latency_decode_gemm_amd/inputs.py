@@ -132,6 +132,11 @@ WORKLOADS_MID = {
     "mid_m": [dict(M=m, K=k, N=n, out="bf16", ldc=ldc)
               for (k, n, ldc) in ((7168, 2112, 4096), (1536, 24576, None), (14336, 7168, None))
               for m in (24, 32, 48, 64)],
+    # the router and ragged-K shapes beyond 16 tokens (fp32 out), where the
+    # crossover to the library GEMM is measured too
+    "mid_router": [dict(M=m, K=k, N=n, out="f32", ldc=None)
+                   for (k, n) in ((7168, 256), (7168, 384), (2880, 128))
+                   for m in (24, 32, 48, 64)],
 }
 
 

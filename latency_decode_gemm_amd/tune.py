@@ -356,7 +356,7 @@ def main():
 
     lib = _capi.lib()
     universe = (inputs.WORKLOADS_F32W["router_f32w"] if f32w else
-                inputs.all_points() + inputs.WORKLOADS_MID["mid_m"])
+                inputs.all_points() + [p for g in inputs.WORKLOADS_MID.values() for p in g])
     check = skg.skinny_gemm_f32w_check_config if f32w else skg.skinny_gemm_check_config
     dispatch = skg.skinny_gemm_f32w_dispatch if f32w else skg.skinny_gemm_dispatch
     run_cfg = skg.skinny_gemm_f32w_with_config if f32w else skg.skinny_gemm_bf16_with_config

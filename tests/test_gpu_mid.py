@@ -81,7 +81,7 @@ def test_mid_forced_config(cfg):
             assert r["ok"], (M, K, N, out_dtype, r)
 
 
-@pytest.mark.parametrize("p", inputs.WORKLOADS_MID["mid_m"],
+@pytest.mark.parametrize("p", inputs.WORKLOADS_MID["mid_m"] + inputs.WORKLOADS_MID["mid_router"],
                          ids=lambda p: f"M{p['M']}_K{p['K']}_N{p['N']}")
 def test_mid_workload_point(p):
     torch = gu.torch_cuda()
@@ -90,7 +90,8 @@ def test_mid_workload_point(p):
     A_bits = inputs.make_a(M, K, N)
     B_bits = gu.cached_b(K, N)
     A, B = gu.operands(A_bits, B_bits, K)
-    buf = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dt = torch.bfloat16 if p["out"] == "bf16" else torch.float32
+    buf = torch.full((M, ldc), float("nan"), dtype=dt, device="cuda")
     skg.skinny_gemm_bf16(A, B, out=buf[:, :N])
     torch.cuda.synchronize()
     r = gu.assess_sampled(buf[:, :N], A_bits, B_bits, K)
