@@ -419,8 +419,9 @@ def load_traffic(dominant_name, config):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of this GEMM is described in DESIGN.md, not run.",
+        print(f"bench.py: the GEMM runs on one GPU (asked for --gpus {args.gpus}); sharding "
+              "it across GPUs (by rows of the weights, or by K with one all-reduce) is not "
+              "implemented.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
