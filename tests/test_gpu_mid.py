@@ -156,3 +156,32 @@ def test_mid_edges(M):
                 r = gu.assess(buf[:, :N], A_bits, B_bits, K)
                 assert r["ok"], (M, K, N, r)
             assert np.isnan(gu.to_f64(buf[:, N:])).all(), (M, K, N)
+
+
+def test_two_streams_mid_tier_and_fp32_weights():
+    """Split-K calls of the middle tier (one pass and two passes) and of the
+    fp32-weight path on two streams at once: each stream has its own
+    workspace, so every result equals its single-stream one."""
+    torch = gu.torch_cuda()
+    p1 = MK(inner=GA, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=2)
+    p2 = MK(backend=P2, inner=RG, split_k=6, row_tiles=1, waves_n=1, waves_k=1, depth=2)
+    pf = MK(inner=skg.SKG_INNER_VALU, split_k=4, row_tiles=1, waves_n=1, waves_k=2, depth=4)
+    A1, B1 = gu.operands(inputs.make_a(40, 7168, 2112), gu.cached_b(7168, 2112), 7168)
+    A2, B2 = gu.operands(inputs.make_a(64, 7168, 256), gu.cached_b(7168, 256), 7168)
+    A3b = inputs.make_a(12, 7168, 384)
+    A3, W3 = gu.operands_f32w(A3b, inputs.make_w_f32(7168, 384), 7168)
+    calls = [lambda s: skg.skinny_gemm_bf16_with_config(A1, B1, p1, stream=s),
+             lambda s: skg.skinny_gemm_bf16_with_config(A2, B2, p2, stream=s),
+             lambda s: skg.skinny_gemm_f32w_with_config(A3, W3, pf, stream=s)]
+    ref = [gu.bits_of(c(None)) for c in calls]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for i in range(12):
+        for j, c in enumerate(calls):
+            s = streams[(i + j) % 2]
+            with torch.cuda.stream(s):
+                outs.append((j, c(s)))
+    torch.cuda.synchronize()
+    for j, o in outs:
+        assert np.array_equal(gu.bits_of(o), ref[j]), j
