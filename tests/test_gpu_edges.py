@@ -236,3 +236,37 @@ def test_stream_read_probe_folds_every_word():
         skg.SKG_ERR_MISALIGNED
     assert lib.skinny_gemm_stream_read(src.data_ptr(), 16, None, None) == skg.SKG_ERR_INVALID_ARG
     assert lib.skinny_gemm_stream_read(None, 0, None, None) == skg.SKG_OK
+
+
+def test_capture_before_warmup_reports_not_warmed():
+    """A split-K call captured on a stream whose workspace was never sized
+    returns SKG_ERR_NOT_WARMED (nothing is allocated or launched while
+    capturing); after skinny_gemm_warmup on that stream the same capture
+    works and its replay equals the eager result."""
+    torch = gu.torch_cuda()
+    M, K, N = 16, 7168, 256
+    cfg = skg.SkgConfig.make(inner=skg.SKG_INNER_MFMA_GA, split_k=4, row_tiles=1, waves_n=1,
+                             waves_k=2, depth=2)
+    A_bits = inputs.make_a(M, K, N)
+    A, B = gu.operands(A_bits, gu.cached_b(K, N), K)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        with pytest.raises(skg.SkinnyGemmError) as e:
+            skg.skinny_gemm_bf16_with_config(A, B, cfg, out=out, stream=s)
+    assert e.value.status == skg.SKG_ERR_NOT_WARMED
+    del g
+    # an eager call on the stream sizes its workspace; capture then works
+    with torch.cuda.stream(s):
+        want = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg, stream=s))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        skg.skinny_gemm_bf16_with_config(A, B, cfg, out=out, stream=s)
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits_of(out), want)
