@@ -166,7 +166,7 @@ std::map<std::pair<int, void *>, Workspace> g_ws;
 // Growing is refused while the stream is capturing a graph.
 int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, Workspace *out) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SKG_ERR_HIP;
+    if (const hipError_t e = hipGetDevice(&dev)) return hip_status(e);
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace &w = g_ws[std::make_pair(dev, (void *)stream)];
     if (w.ws_floats >= need_floats && w.n_tickets >= need_tickets) {
@@ -174,24 +174,26 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
         return SKG_OK;
     }
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SKG_ERR_HIP;
+    if (const hipError_t e = hipStreamIsCapturing(stream, &cap)) return hip_status(e);
     if (cap != hipStreamCaptureStatusNone) return SKG_ERR_NOT_WARMED;
     // earlier kernels on this stream may still use the old buffers
-    if (hipStreamSynchronize(stream) != hipSuccess) return SKG_ERR_HIP;
+    if (const hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
     const size_t nf = std::max(need_floats, w.ws_floats);
     const size_t nt = std::max(need_tickets, w.n_tickets);
     float *ws = nullptr;
     unsigned *tk = nullptr;
-    if (hipMalloc(&ws, std::max<size_t>(nf, 1) * sizeof(float)) != hipSuccess) return SKG_ERR_HIP;
-    if (hipMalloc(&tk, std::max<size_t>(nt, 1) * sizeof(unsigned)) != hipSuccess) {
+    if (const hipError_t e = hipMalloc(&ws, std::max<size_t>(nf, 1) * sizeof(float)))
+        return hip_status(e);
+    if (const hipError_t e = hipMalloc(&tk, std::max<size_t>(nt, 1) * sizeof(unsigned))) {
         (void)hipFree(ws);
-        return SKG_ERR_HIP;
+        return hip_status(e);
     }
-    if (hipMemset(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
+    hipError_t e = hipMemset(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
         (void)hipFree(ws);
         (void)hipFree(tk);
-        return SKG_ERR_HIP;
+        return hip_status(e);
     }
     if (w.ws) (void)hipFree(w.ws);
     if (w.tickets) (void)hipFree(w.tickets);
@@ -513,21 +515,20 @@ int warmup_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_value
     }
     uint16_t *a = nullptr, *b = nullptr;
     float *c = nullptr;
-    if (hipMalloc(&a, max_a * 2) != hipSuccess) return SKG_ERR_HIP;
+    if (const hipError_t e = hipMalloc(&a, max_a * 2)) return hip_status(e);
     const size_t b_bytes = max_b * (f32w ? 4 : 2);  // weights: bf16 or fp32
-    if (hipMalloc(&b, b_bytes) != hipSuccess) {
+    if (const hipError_t e = hipMalloc(&b, b_bytes)) {
         (void)hipFree(a);
-        return SKG_ERR_HIP;
+        return hip_status(e);
     }
-    if (hipMalloc(&c, max_c * 4) != hipSuccess) {
+    if (const hipError_t e = hipMalloc(&c, max_c * 4)) {
         (void)hipFree(a);
         (void)hipFree(b);
-        return SKG_ERR_HIP;
+        return hip_status(e);
     }
-    int rc = SKG_OK;
-    if (hipMemsetAsync(a, 0, max_a * 2, stream) != hipSuccess ||
-        hipMemsetAsync(b, 0, b_bytes, stream) != hipSuccess)
-        rc = SKG_ERR_HIP;
+    hipError_t e = hipMemsetAsync(a, 0, max_a * 2, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(b, 0, b_bytes, stream);
+    int rc = hip_status(e);
     for (auto &t : todo) {
         if (rc != SKG_OK) break;
         const int M = t.second.first, K = t.second.second;
@@ -537,7 +538,8 @@ int warmup_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_value
         rc = run(a, b, c, M, g.rows_per_wg, K, ld, ld, g.rows_per_wg, SKG_OUT_F32, stream,
                  t.first, nullptr, nullptr, f32w);
     }
-    if (hipStreamSynchronize(stream) != hipSuccess && rc == SKG_OK) rc = SKG_ERR_HIP;
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess && rc == SKG_OK) rc = hip_status(e);
     (void)hipFree(a);
     (void)hipFree(b);
     (void)hipFree(c);

@@ -491,3 +491,37 @@ def test_log_env_prints_the_choice_once_per_shape():
     cfg = skg.skinny_gemm_dispatch(4, 7168, 256)
     assert len(lines) == 1, r.stderr
     assert f"backend {cfg.backend} inner {cfg.inner} split_k {cfg.split_k}" in lines[0]
+
+
+def test_hip_errors_are_recorded_on_the_workspace_path():
+    """Without a GPU every HIP call fails. A split-K GEMM call and a warm-up
+    both reach the workspace code first; each returns SKG_ERR_HIP, and
+    skinny_gemm_last_hip_error() then holds the runtime's code, not 0."""
+    import subprocess
+    import sys
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("needs a machine without a GPU: the call passes placeholder pointers")
+    assert skg.skinny_gemm_dispatch(16, 7168, 256).split_k > 1
+    code = (
+        "import ctypes\n"
+        "from latency_decode_gemm_amd import _capi\n"
+        "lib = _capi.lib()\n"
+        "print('start', lib.skinny_gemm_last_hip_error())\n"
+        "st = lib.skinny_gemm_bf16(0x100000, 0x100000, 0x100000, 16, 256, 7168, 7168, 7168,"
+        " 256, 0, None)\n"
+        "print('gemm', st, lib.skinny_gemm_last_hip_error())\n"
+        "kn = (ctypes.c_int * 2)(7168, 256)\n"
+        "ms = (ctypes.c_int * 1)(16)\n"
+        "n = ctypes.c_int(0)\n"
+        "st = lib.skinny_gemm_warmup(kn, 1, ms, 1, None, ctypes.byref(n))\n"
+        "print('warmup', st, lib.skinny_gemm_last_hip_error())\n")
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       env=env, timeout=120)
+    assert r.returncode == 0, r.stderr
+    got = {ln.split()[0]: [int(x) for x in ln.split()[1:]] for ln in r.stdout.splitlines()}
+    assert got["start"] == [0]
+    for what in ("gemm", "warmup"):
+        st, err = got[what]
+        assert st == skg.SKG_ERR_HIP, (what, got)
+        assert err != 0, (what, got)
