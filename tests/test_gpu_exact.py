@@ -49,6 +49,15 @@ FAMILIES = [
 ]
 
 
+def _first_fit(cfg, M, shapes):
+    """The first (K, N) in shapes that the configuration runs (all fit the
+    dispatch table's choice)."""
+    for K, N in shapes:
+        if cfg is None or skg.skinny_gemm_check_config(M, K, N, cfg):
+            return K, N
+    raise AssertionError(f"no test shape fits {cfg}")
+
+
 def _m_for(cfg, m):
     """Tokens for a test shape: the activation-ring VALU kernel takes M <= 8."""
     return min(m, 8) if cfg is not None and cfg.inner == VG else m
@@ -104,14 +113,14 @@ def test_one_hot(cfg):
 def test_identity(cfg):
     torch = gu.torch_cuda()
     rng = np.random.default_rng(8)
-    K = N = 256
     M = _m_for(cfg, 16)
+    # the smallest square that the configuration fits (a K split needs
+    # enough K steps per slice)
+    K = N = _first_fit(cfg, M, [(k, k) for k in (256, 1024, 2048)])[0]
     A_bits = _dyadic(rng, (M, K), -127, 127, 2.0 ** -3)
     B_bits = np.zeros((N, K), dtype=np.uint16)
     B_bits[np.arange(K), np.arange(K)] = 0x3F80
     A, B = gu.operands(A_bits, B_bits, K)
-    if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
-        pytest.skip("configuration does not fit this shape")
     for odt in (torch.float32, torch.bfloat16):
         C = _gemm(A, B, cfg, odt)
         torch.cuda.synchronize()
@@ -121,18 +130,23 @@ def test_identity(cfg):
 @pytest.mark.parametrize("cfg", FAMILIES, ids=_fid)
 def test_constant_closed_form(cfg):
     torch = gu.torch_cuda()
+    ran = 0
+    # 1 * 2^-6 summed K times, and -1.5 * 0.75 summed K times
     for K, ab, bb, want in ((7168, 0x3F80, 0x3C80, 112.0), (2880, 0x3F80, 0x3C80, 45.0),
-                            (1536, 0x3F80, 0x3C80, 24.0), (7168, 0xBFC0, 0x3F40, -8064.0)):
+                            (1536, 0x3F80, 0x3C80, 24.0), (7168, 0xBFC0, 0x3F40, -8064.0),
+                            (512, 0x3F80, 0x3C80, 8.0), (256, 0xBFC0, 0x3F40, -288.0)):
         M, N = 5, 40
+        if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
+            continue
+        ran += 1
         A_bits = np.full((M, K), ab, dtype=np.uint16)
         B_bits = np.full((N, K), bb, dtype=np.uint16)
         A, B = gu.operands(A_bits, B_bits, K)
-        if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
-            continue
         for odt in (torch.float32, torch.bfloat16):
             C = _gemm(A, B, cfg, odt)
             torch.cuda.synchronize()
             assert np.all(gu.to_f64(C) == want), (K, odt)
+    assert ran >= 2, "fewer than two constant cases fit this configuration"
 
 
 @pytest.mark.parametrize("cfg", FAMILIES, ids=_fid)
@@ -141,7 +155,10 @@ def test_bf16_rounding_is_nearest_even(cfg):
     exact value (the oracle's rounding), bit for bit; ties included."""
     torch = gu.torch_cuda()
     rng = np.random.default_rng(9)
-    M, K, N = _m_for(cfg, 16), 48, 96
+    # |A| <= 16, |B| <= 255 * 2^-8: every partial sum over K <= 4096 terms is
+    # a multiple of 2^-8 below 2^16, exact in fp32 in any order
+    M = _m_for(cfg, 16)
+    K, N = _first_fit(cfg, M, [(48, 96), (384, 96), (1536, 96), (4096, 96)])
     A_bits = _dyadic(rng, (M, K), -16, 16, 1.0)
     B_bits = _dyadic(rng, (N, K), -255, 255, 2.0 ** -8)
     # hand-made ties in the first columns: 1 + 2^-8 -> 1.0, 1 + 3*2^-8 -> 1 + 2^-6
@@ -152,8 +169,6 @@ def test_bf16_rounding_is_nearest_even(cfg):
     B_bits[1, :] = 0
     B_bits[1, :2] = [0x3F80, oracle.round_bf16(3 * 2.0 ** -8)]
     A, B = gu.operands(A_bits, B_bits, K)
-    if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
-        pytest.skip("configuration does not fit this shape")
     C = _gemm(A, B, cfg, torch.bfloat16)
     torch.cuda.synchronize()
     ref = oracle.gemm_f64(A_bits, B_bits, K)
