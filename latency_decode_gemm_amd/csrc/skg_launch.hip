@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <mutex>
 #include <set>
+#include <utility>
 
 #include "skg_device.h"
 
@@ -170,11 +171,14 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
     KernelPtr fn = find_kernel(cfg.inner, p.M, cfg.row_tiles, cfg.depth, p.w_f32 != 0);
     if (!fn) return hipErrorInvalidValue;
     if (g.lds_bytes > 64 * 1024) {
-        // allow this kernel the full LDS of a CU (once per kernel)
+        // allow this kernel the full LDS of a CU (once per kernel and
+        // device: the attribute belongs to the kernel as loaded on one device)
+        int dev = 0;
+        if (const hipError_t e = hipGetDevice(&dev)) return e;
         static std::mutex mu;
-        static std::set<KernelPtr> done;
+        static std::set<std::pair<int, KernelPtr>> done;
         std::lock_guard<std::mutex> lock(mu);
-        if (!done.count(fn)) {
+        if (!done.count(std::make_pair(dev, fn))) {
             // resolving the device function loads the kernel's code object,
             // which the runtime may otherwise defer to the first launch
             // (raising the limit of a kernel whose code object is not loaded
@@ -185,7 +189,7 @@ hipError_t launch(const KParams &p, const Geometry &g, const skg_config &cfg,
             if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                     kMaxLdsBytes) == hipSuccess)
-                done.insert(fn);
+                done.insert(std::make_pair(dev, fn));
             (void)hipGetLastError();  // neither failure belongs to the launch
         }
     }
