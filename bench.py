@@ -167,22 +167,11 @@ def next_copy(pt):
     return B
 
 
-def check_parity(oracle, acceptance, pt, bits_B, torch):
-    """Sampled outputs against the oracle (all M rows, up to 64 columns)."""
-    import numpy as np
-    C = pt.Cbuf[:, :pt.N].float().cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(0)
-    ns = np.sort(rng.choice(pt.N, size=min(64, pt.N), replace=False))
-    ms = np.repeat(np.arange(pt.M), ns.size)
-    nn = np.tile(ns, pt.M)
-    an = acceptance.row_norms(oracle.bf16_decode(pt.A_bits), pt.K)
-    if pt.f32w:
-        ref = oracle.gemm_f32w_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
-        bn = acceptance.row_norms(bits_B[ns].astype(np.float64), pt.K)
-    else:
-        ref = oracle.gemm_points(pt.A_bits, bits_B, pt.K, ms, nn).reshape(pt.M, ns.size)
-        bn = acceptance.row_norms(oracle.bf16_decode(bits_B[ns]), pt.K)
-    return acceptance.assess(C[:, ns], ref, an, bn, pt.out)
+def check_parity(pt, bits_B, torch):
+    """Sampled outputs (all M rows, up to 64 columns) against a plain float64
+    product of the decoded inputs."""
+    from latency_decode_gemm_amd import spot_check
+    return spot_check.sampled_check(torch, pt.A_bits, bits_B, pt.Cbuf, pt.K, pt.out)
 
 
 def time_points_graph(torch, lib, pts, stream, calls=200, warm=20):
@@ -515,17 +504,15 @@ def main():
         graph_ms = g0.elapsed_time(g1) / (reps * GRAPH_STEPS)
         del g
 
-    # results are still right after the timed loop (sampled oracle check)
+    # results are still right after the timed loop (sampled float64 check)
     bad = []
     if not args.only:
-        import oracle
-        from oracle import acceptance
         for pt in pts:
-            r = check_parity(oracle, acceptance, pt, bpool.bits[pt.key()], torch)
+            r = check_parity(pt, bpool.bits[pt.key()], torch)
             if not r["ok"]:
                 bad.append((pt.name(), r))
     if bad:
-        print(f"bench.py: results do not match the oracle: {bad}", file=sys.stderr)
+        print(f"bench.py: results do not match the float64 check: {bad}", file=sys.stderr)
         sys.exit(1)
 
     if args.copy_probe_mb:
