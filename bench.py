@@ -17,7 +17,11 @@ Prints ONE JSON line:
                  divided by its average kernel duration, from HIP events that
                  its dispatches record (skinny_gemm_bf16_timed) on every step
                  of the timed region;
-  cpu_baseline = the CPU oracle timed on this host over the same workload.
+  cpu_baseline = the CPU oracle timed on this host over the same workload;
+  gated_points_kernel_us = after the timed region, the median kernel time
+                 of every point with N*K >= 7168*2112 (qkv_a-style, wide,
+                 deep; the points the bandwidth target covers) and its
+                 fraction of the 8 TB/s peak.
 ``--workload router_f32w`` measures the router GEMM over fp32 weights
 (skinny_gemm_f32w; weight bytes 4*N*K) the same way, ``--workload mid_m`` the
 middle tier (16 < M <= 64) on the projection shapes.
@@ -87,6 +91,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph (GRAPH_STEPS steps "
                          "captured with rotating weight copies): ms_per_step_graph")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the per-point report of the points the bandwidth target "
+                         "covers (N*K >= 7168*2112), timed after the headline region")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -252,6 +259,43 @@ def time_points_eager(torch, lib, pts, stream, calls=200, warm=20):
     return res
 
 
+GATED_NK = 7168 * 2112  # the bandwidth target applies to N * K at least this
+
+
+def gated_points_report(torch, skg, lib, inputs, stream, bpool, pts, calls=100, warm=10):
+    """Every workload point with N * K >= 7168 * 2112 (qkv_a-style, wide and
+    deep, M <= 16): median kernel time over `calls` dispatches that record
+    their own start and end (skinny_gemm_bf16_timed), weights rotated past
+    the Infinity Cache as in the timed region, and the weight bytes 2NK per
+    second as a fraction of the 8 TB/s peak.  Run after the timed region, so
+    it does not change ms_per_step."""
+    h = stream.cuda_stream
+    spec = [p for p in inputs.all_points() if p["N"] * p["K"] >= GATED_NK]
+    have = {pt.name(): pt for pt in pts}
+    shapes = [(K, N, False) for (K, N) in dict.fromkeys((p["K"], p["N"]) for p in spec)
+              if (K, N, False) not in bpool.copies]
+    extra = BPool(torch, inputs, shapes) if shapes else None
+    out = {}
+    ev = [(skg.HipEvent(), skg.HipEvent()) for _ in range(calls)]
+    for p in spec:
+        key = (p["K"], p["N"], False)
+        pool = bpool if key in bpool.copies else extra
+        pt = Point(torch, skg, inputs, p, pool)
+        pt = have.get(pt.name(), pt)
+        skg.skinny_gemm_warmup([(pt.K, pt.N)], [pt.M], stream=stream)
+        for _ in range(warm):
+            call(lib, pt, next_copy(pt), h)
+        for i in range(calls):
+            call(lib, pt, next_copy(pt), h, ev[i])
+        torch.cuda.synchronize()
+        us = median([a.elapsed_ms(b) * 1000.0 for a, b in ev])
+        gbs = pt.weight_bytes / us / 1e3
+        out[pt.name()] = {"kernel_us": round(us, 3), "weight_GBps": round(gbs, 1),
+                          "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+    del extra
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -314,6 +358,7 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
 
     shapes = list(dict.fromkeys(key_of(p) for p in spec))
     table = {}
+    cpu_jobs = []  # (point, oracle function, A bits, B bits, K), timed at the end
     order = 0
     sink = torch.zeros(512, dtype=torch.int32, device="cuda")
     for (K, N, f32w) in shapes:
@@ -376,18 +421,27 @@ def points_report(torch, np, skg, lib, inputs, oracle, stream, calls=200, warm=2
             k_us = e["kernel_us_events_median"]
             e["weight_GBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3, 1)
             e["frac_of_8TBps_kernel_events"] = round(pt.weight_bytes / k_us / 1e3 / PEAK_HBM_GBS, 4)
-            # CPU oracle on this point
-            bits_B = bp.bits[(K, N, f32w)]
-            for threads, key in ((oracle.default_threads(), "cpu_all_cores"), (1, "cpu_one_core")):
-                ts = []
-                for rep in range(4):
-                    t0 = time.perf_counter()
-                    oracle_gemm(oracle, pt)(pt.A_bits, bits_B, K, threads=threads)
-                    ts.append(time.perf_counter() - t0)
-                e[key] = {"us_per_call": round(median(ts[1:]) * 1e6, 1), "threads": threads}
+            cpu_jobs.append((pt.name(), oracle_gemm(oracle, pt), pt.A_bits, bp.bits[(K, N, f32w)],
+                             K))
         del ps, bp, hot
         torch.cuda.empty_cache()
         print(f"points: K={K} N={N} done", file=sys.stderr, flush=True)
+    # CPU oracle per point, after all GPU work (host threads of the GPU
+    # runtime no longer compete with the oracle's), the thread pool warmed
+    # once first; per point one warm-up call, then the median of 3
+    torch.cuda.synchronize()
+    if cpu_jobs:
+        name, fn, a_bits, b_bits, K = cpu_jobs[0]
+        fn(a_bits, b_bits, K, threads=oracle.default_threads())
+    for name, fn, a_bits, b_bits, K in cpu_jobs:
+        e = table[name]
+        for threads, key in ((oracle.default_threads(), "cpu_all_cores"), (1, "cpu_one_core")):
+            ts = []
+            for rep in range(4):
+                t0 = time.perf_counter()
+                fn(a_bits, b_bits, K, threads=threads)
+                ts.append(time.perf_counter() - t0)
+            e[key] = {"us_per_call": round(median(ts[1:]) * 1e6, 1), "threads": threads}
     return table
 
 
@@ -524,6 +578,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    gated = None
+    if not args.no_gated and not args.only and not any(p.f32w for p in pts):
+        gated = gated_points_report(torch, skg, lib, inputs, stream, bpool, pts)
+
     traffic = load_traffic(dom.name(), dom.cfg.as_dict())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -552,6 +610,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if gated is not None:
+        line["gated_points_kernel_us"] = gated
+        line["gated_points_min_frac"] = min(v["frac_of_8TBps"] for v in gated.values())
     if args.points_out:
         del pts, bpool
         torch.cuda.empty_cache()

@@ -42,6 +42,15 @@
  *   - Thread safety: all entry points may be called from several host
  *     threads.  Calls on different streams use different workspaces; calls
  *     on one stream are ordered by the stream.
+ *   - Split-K workspace: the library allocates one per (device, stream) the
+ *     first time a configuration with a K split runs there (or in
+ *     skinny_gemm_warmup), grows it when a later call needs more, and never
+ *     frees a workspace it has replaced, so a graph captured earlier keeps
+ *     valid addresses.  A captured graph uses the workspace of the stream
+ *     it was captured on: replaying it while other split-K work on that
+ *     workspace runs (calls on the capture stream, or another replay on
+ *     another stream) races; replay it on the capture stream.  Growing is
+ *     refused during capture (SKG_ERR_NOT_WARMED): warm up first.
  *   - Logging: with SKINNY_GEMM_LOG=1 in the environment, the first GEMM call
  *     of each (weight type, M, K, N) prints the chosen configuration to
  *     stderr.  No environment variable changes the dispatch.
@@ -263,7 +272,10 @@ int skinny_gemm_f32w_warmup(const int *kn_pairs, int n_shapes, const int *m_valu
  * failure reports the runtime's own code here. */
 int skinny_gemm_last_hip_error(void);
 
-/* 1 if a gfx950 device is current and the library's kernels load, else 0. */
+/* 1 if a gfx950 device is current and the library's kernels load, else 0.
+ * The counterpart of is_available in the ll_bf16.py excerpt of the PR #42562
+ * page (section 关键源码片段), which tells the router gate whether the
+ * kernel path can run on the current device before it is chosen. */
 int skinny_gemm_available(void);
 
 /* Measurement aid, not part of the GEMM: streams `bytes` bytes from the

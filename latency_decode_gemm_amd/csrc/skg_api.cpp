@@ -163,7 +163,13 @@ std::mutex g_ws_mu;
 std::map<std::pair<int, void *>, Workspace> g_ws;
 
 // The split-K workspace of (current device, stream), grown if needed.
-// Growing is refused while the stream is capturing a graph.
+// Growing is refused while the stream is capturing a graph.  A workspace that
+// has been replaced is never freed: a graph captured earlier on this stream
+// holds its addresses in its kernel arguments and may be replayed at any time,
+// so every buffer stays allocated until the process ends (the sizes only grow,
+// so at most a few buffers per stream are ever retired).  The new tickets are
+// zeroed in stream order before the first kernel that uses them; no host or
+// device synchronisation is needed, since no buffer is freed.
 int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, Workspace *out) {
     int dev = 0;
     if (const hipError_t e = hipGetDevice(&dev)) return hip_status(e);
@@ -176,8 +182,6 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (const hipError_t e = hipStreamIsCapturing(stream, &cap)) return hip_status(e);
     if (cap != hipStreamCaptureStatusNone) return SKG_ERR_NOT_WARMED;
-    // earlier kernels on this stream may still use the old buffers
-    if (const hipError_t e = hipStreamSynchronize(stream)) return hip_status(e);
     const size_t nf = std::max(need_floats, w.ws_floats);
     const size_t nt = std::max(need_tickets, w.n_tickets);
     float *ws = nullptr;
@@ -188,15 +192,13 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
         (void)hipFree(ws);
         return hip_status(e);
     }
-    hipError_t e = hipMemset(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
+    // (the stream is not capturing here, so this memset is never part of a graph)
+    if (const hipError_t e =
+            hipMemsetAsync(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned), stream)) {
         (void)hipFree(ws);
         (void)hipFree(tk);
         return hip_status(e);
     }
-    if (w.ws) (void)hipFree(w.ws);
-    if (w.tickets) (void)hipFree(w.tickets);
     w.ws = ws;
     w.ws_floats = nf;
     w.tickets = tk;

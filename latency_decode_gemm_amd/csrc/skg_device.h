@@ -34,13 +34,12 @@
 //  * Cross-wave (waves_k > 1): partials go through LDS (double-buffered per
 //    row block) and wave 0 adds them in wave order.  Cross-workgroup
 //    (split_k > 1): each workgroup stores its fp32 partial tile with
-//    agent-scope atomic stores, waits for them, and takes a ticket with one
-//    agent-scope atomic add; the workgroup that draws the last ticket reads the
-//    split_k partials with agent-scope atomic loads, adds them in split order,
-//    writes C and resets the ticket.  These accesses are coherent across the
-//    XCDs' L2s without any L2 write-back or invalidate.  Nothing waits for
-//    another workgroup, and no summation order depends on timing, so results
-//    are bit-reproducible.
+//    agent-scope atomic stores and takes a ticket with one agent-scope
+//    release add (one per workgroup, after a workgroup barrier); the
+//    workgroup that draws the last ticket performs an agent-scope acquire,
+//    reads the split_k partials, adds them in split order, writes C and
+//    resets the ticket.  Nothing waits for another workgroup, and no
+//    summation order depends on timing, so results are bit-reproducible.
 //  * Epilogue: fp32 stores, or bf16 round-to-nearest-even, at C[m*ldc + n];
 //    other bytes of C are never written.
 #pragma once
@@ -338,18 +337,34 @@ __device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start,
     }
 }
 
-// Called by every thread of the workgroup once this workgroup's partials of
-// row block rb are stored (ws_store) and complete (s_waitcnt) in the waves that
-// stored them.  The workgroup that draws the last ticket adds the split_k
+// Workgroup barrier with release/acquire fences over every address space, so
+// that each thread's earlier global stores happen before whatever any thread
+// of the workgroup does after it.
+__device__ __forceinline__ void wg_barrier_all() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Called by every thread of the workgroup once its partials of row block rb
+// are stored (ws_store).  The ordering is the language's, not the hardware's:
+// the workgroup barrier orders every thread's partial stores before thread 0's
+// ticket, which is an agent-scope release (it publishes them to the other
+// workgroups); the workgroup that draws the last ticket performs an
+// agent-scope acquire fence before the barrier that lets its threads read the
+// partials, so every other workgroup's release happens before those reads.
+// Only the last arriver pays for the acquire.  That workgroup adds the split_k
 // partials ws[rb][0..S)[m][rl] in split order and writes C.
 __device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsigned *flag) {
-    lds_barrier();
+    wg_barrier_all();
     if (threadIdx.x == 0) {
-        const unsigned t = __hip_atomic_fetch_add(&p.tickets[rb], 1u, __ATOMIC_RELAXED,
+        const unsigned t = __hip_atomic_fetch_add(&p.tickets[rb], 1u, __ATOMIC_RELEASE,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-        *flag = (t == (unsigned)(p.split_k - 1)) ? 1u : 0u;
+        const bool last = t == (unsigned)(p.split_k - 1);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *flag = last ? 1u : 0u;
     }
-    lds_barrier();
+    wg_barrier_all();
     if (*flag) {
         const int NB = p.rows_per_wg;
         const int total = p.M * NB;
@@ -432,10 +447,7 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
                 ws_store(part + m * NB, v);
             }
         }
-        if (p.split_k > 1 && !p.two_pass) {
-            __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores complete
-            splitk_complete(p, rb, flag);
-        }
+        if (p.split_k > 1 && !p.two_pass) splitk_complete(p, rb, flag);
     }
 }
 

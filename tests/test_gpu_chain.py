@@ -1,9 +1,11 @@
 """A decode layer's chain of GEMMs captured in one HIP graph (GPU): the
 router over fp32 weights, the qkv_a-style projection into its strided
 buffer, the wide and the deep projection at M = 4, and a middle-tier call;
-warm-up first (so split-K workspaces exist), then capture.  Every replay,
-with eager work between the replays, equals the eager results bit for bit,
-and the padding columns of the strided buffer stay untouched."""
+warm-up first (so split-K workspaces exist), then capture.  The eager result
+of every member is checked against the oracle (all of it, or every row and
+sampled columns at the largest shapes), and every replay, with eager work
+between the replays, equals those results bit for bit, with the padding
+columns of the strided buffer untouched."""
 import numpy as np
 import pytest
 
@@ -19,7 +21,7 @@ def test_decode_chain_graph_replays_match_eager():
     s = torch.cuda.Stream()
     chain = inputs.WORKLOADS_CHAIN["decode_chain"] + [
         dict(M=32, K=7168, N=2112, out="bf16", ldc=4096)]
-    calls = []
+    calls, refs = [], []
     for p in chain:
         M, K, N = p["M"], p["K"], p["N"]
         f32w = p.get("w") == "f32"
@@ -35,12 +37,24 @@ def test_decode_chain_graph_replays_match_eager():
         dt = torch.bfloat16 if p["out"] == "bf16" else torch.float32
         buf = torch.full((M, p["ldc"] or N), float("nan"), dtype=dt, device="cuda")
         calls.append((f32w, A, W, buf, N))
+        refs.append((f32w, A_bits, inputs.make_w_f32(K, N) if f32w else gu.cached_b(K, N), K))
     fn = {True: skg.skinny_gemm_f32w, False: skg.skinny_gemm_bf16}
     with torch.cuda.stream(s):
         for (f32w, A, W, buf, N) in calls:
             fn[f32w](A, W, out=buf[:, :N], stream=s)
     torch.cuda.synchronize()
     eager = [gu.bits_of(buf) for (_, _, _, buf, _) in calls]
+    for (f32w, A_bits, W_bits, K), (_, _, _, buf, N) in zip(refs, calls):
+        C = buf[:, :N]
+        if f32w:
+            r = gu.assess_f32w(C, A_bits, W_bits, K)
+        elif N * K > 2112 * 7168:
+            r = gu.assess_sampled(C, A_bits, W_bits, K)
+        else:
+            r = gu.assess(C, A_bits, W_bits, K)
+        assert r["ok"], (buf.shape, N, K, r)
+        if buf.shape[1] > N:
+            assert np.isnan(gu.to_f64(buf[:, N:])).all()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for (f32w, A, W, buf, N) in calls:

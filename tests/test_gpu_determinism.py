@@ -33,7 +33,7 @@ def test_repeated_calls_identical(shape):
 
 def test_default_equals_explicit_dispatch_config():
     torch = gu.torch_cuda()
-    for p in inputs.all_points()[:18]:
+    for p in inputs.all_points():
         A, B = _problem(p["M"], p["K"], p["N"])
         cfg = skg.skinny_gemm_dispatch(p["M"], p["K"], p["N"])
         c1 = skg.skinny_gemm_bf16(A, B)
@@ -59,11 +59,40 @@ def test_split_k_forced_is_reproducible():
                     row_tiles=1, waves_n=1, waves_k=1, depth=4))]
     for M, cfg in cases:
         A, B = _problem(M, 7168, 256)
-        ref = gu.bits_of(skg.skinny_gemm_bf16_with_config(A, B, cfg))
-        for _ in range(100):
-            c = skg.skinny_gemm_bf16_with_config(A, B, cfg)
+        _repeat_identical(lambda out: skg.skinny_gemm_bf16_with_config(A, B, cfg, out=out),
+                          M, 256, 1000, (M, cfg))
+
+
+def _repeat_identical(call, M, N, reps, what, batch=50):
+    """Runs call(out) reps times, batch outputs at a time, and stops at the
+    first output that differs bit for bit from the first one."""
+    torch = gu.torch_cuda()
+    ref = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    call(ref)
+    outs = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(batch)]
+    refi = ref.view(torch.int32)
+    done = 0
+    while done < reps:
+        n = min(batch, reps - done)
+        for o in outs[:n]:
+            o.fill_(float("nan"))
+        for o in outs[:n]:
+            call(o)
         torch.cuda.synchronize()
-        assert np.array_equal(gu.bits_of(c), ref), (M, cfg)
+        for i, o in enumerate(outs[:n]):
+            assert torch.equal(o.view(torch.int32), refi), (what, "call", done + i + 1)
+        done += n
+
+
+@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("N", [256, 384])
+def test_router_split_k_thousands_of_calls(M, N):
+    """The router points that dispatch a single-pass K split (the ticket
+    and last-arriver sum): 2000 calls, every one bit-identical to the first."""
+    A, B = _problem(M, 7168, N)
+    cfg = skg.skinny_gemm_dispatch(M, 7168, N)
+    assert cfg.split_k > 1 and cfg.backend != skg.SKG_BACKEND_SPLITK_2PASS, cfg
+    _repeat_identical(lambda out: skg.skinny_gemm_bf16(A, B, out=out), M, N, 2000, (M, N, cfg))
 
 
 def test_warmup_then_same_bits():

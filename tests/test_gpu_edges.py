@@ -270,3 +270,55 @@ def test_capture_before_warmup_reports_not_warmed():
     g.replay()
     torch.cuda.synchronize()
     assert np.array_equal(gu.bits_of(out), want)
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured after a small warm-up keeps working after a larger
+    split-K shape grows the same stream's workspace: the replaced workspace
+    stays allocated (the graph's kernels still address it), so every replay
+    still matches the oracle and the eager result, with eager calls on the
+    grown workspace between the replays."""
+    torch = gu.torch_cuda()
+    K = 7168
+    small, large = (8, 256), (16, 384)  # router points: split 2, then split 4
+    c_small = skg.skinny_gemm_dispatch(small[0], K, small[1])
+    c_large = skg.skinny_gemm_dispatch(large[0], K, large[1])
+    assert c_small.split_k > 1 and c_large.split_k > 1
+    assert (skg.skinny_gemm_workspace_bytes(large[0], K, large[1], c_large)
+            > skg.skinny_gemm_workspace_bytes(small[0], K, small[1], c_small))
+    s = torch.cuda.Stream()
+    probs = {}
+    for (M, N) in (small, large):
+        A_bits = inputs.make_a(M, K, N)
+        B_bits = gu.cached_b(K, N)
+        probs[(M, N)] = (A_bits, B_bits) + gu.operands(A_bits, B_bits, K)
+    # a fresh stream: the small warm-up sizes its workspace for the small
+    # shape only
+    with torch.cuda.stream(s):
+        skg.skinny_gemm_warmup([(K, small[1])], [small[0]], stream=s)
+    A_bits, B_bits, A, B = probs[small]
+    out = torch.empty(small, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        want = gu.bits_of(skg.skinny_gemm_bf16(A, B, stream=s))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        skg.skinny_gemm_bf16(A, B, out=out, stream=s)
+    # grow the workspace of the same stream (the old one is retired, not freed)
+    with torch.cuda.stream(s):
+        skg.skinny_gemm_warmup([(K, large[1])], [large[0]], stream=s)
+    La_bits, Lb_bits, LA, LB = probs[large]
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        r = gu.assess(out, A_bits, B_bits, K)
+        assert r["ok"], (i, r)
+        assert np.array_equal(gu.bits_of(out), want), i
+        # eager work on the grown workspace between the replays, on the same stream
+        with torch.cuda.stream(s):
+            big = skg.skinny_gemm_bf16(LA, LB, stream=s)
+        torch.cuda.synchronize()
+        r = gu.assess(big, La_bits, Lb_bits, K)
+        assert r["ok"], (i, r)

@@ -86,27 +86,40 @@ def _dyadic(rng, shape, lo, hi, scale):
 
 @pytest.mark.parametrize("cfg", FAMILIES, ids=_fid)
 def test_one_hot(cfg):
+    """Every family runs every one-hot position of at least one ragged K
+    (main steps, the last full chunk, the chunk that straddles K), in groups
+    of as many tokens as the family takes; each of K = 2880, 1531 and 1003
+    where the family fits it."""
     torch = gu.torch_cuda()
     rng = np.random.default_rng(7)
+    N = 48
+    ran = {}
     for K, ks in ((2880, [0, 7, 8, 127, 128, 2047, 2048, 2559, 2560, 2687, 2688, 2815,
                           2816, 2871, 2872, 2879]),
+                  (1531, [0, 7, 8, 127, 128, 1023, 1024, 1407, 1408, 1519, 1520, 1523,
+                          1524, 1527, 1528, 1530]),
                   (1003, [0, 1, 8, 500, 999, 1000, 1001, 1002])):
         ld = gu.round8(K)
-        M = len(ks)
-        N = 48
-        A_bits = np.zeros((M, ld), dtype=np.uint16)
-        for m, k in enumerate(ks):
-            A_bits[m, k] = 0x3F80
         B_bits = np.full((N, ld), 0x7FC1, dtype=np.uint16)
         B_bits[:, :K] = _dyadic(rng, (N, K), -255, 255, 2.0 ** -7)
-        A, B = gu.operands(A_bits, B_bits, K)
-        if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
-            continue
-        C = _gemm(A, B, cfg, torch.float32)
-        torch.cuda.synchronize()
-        want = oracle.bf16_decode(B_bits[:, ks]).T
-        got = gu.to_f64(C)
-        assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+        per = _m_for(cfg, len(ks))
+        for g0 in range(0, len(ks), per):
+            kg = ks[g0:g0 + per]
+            M = len(kg)
+            if cfg is not None and not skg.skinny_gemm_check_config(M, K, N, cfg):
+                continue
+            A_bits = np.zeros((M, ld), dtype=np.uint16)
+            for m, k in enumerate(kg):
+                A_bits[m, k] = 0x3F80
+            A, B = gu.operands(A_bits, B_bits, K)
+            C = _gemm(A, B, cfg, torch.float32)
+            torch.cuda.synchronize()
+            want = oracle.bf16_decode(B_bits[:, kg]).T
+            got = gu.to_f64(C)
+            assert np.array_equal(got, want), (K, kg, np.argwhere(got != want)[:8])
+            ran[K] = ran.get(K, 0) + M
+    # every position of some ragged K must have run (none may pass vacuously)
+    assert ran.get(2880, 0) == 16 or ran.get(1531, 0) == 16, f"one-hot positions run: {ran}"
 
 
 @pytest.mark.parametrize("cfg", FAMILIES, ids=_fid)
