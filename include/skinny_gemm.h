@@ -41,7 +41,8 @@
  *     device memory unchanged.
  *   - Thread safety: all entry points may be called from several host
  *     threads.  Calls on different streams use different workspaces; calls
- *     on one stream are ordered by the stream.
+ *     on one stream are ordered by the stream.  (skinny_gemm_bf16_noalloc
+ *     is the exception: it uses one workspace per GPU.)
  *   - Split-K workspace: the library allocates one per (device, stream) the
  *     first time a configuration with a K split runs there (or in
  *     skinny_gemm_warmup), grows it when a later call needs more, and never
@@ -76,7 +77,10 @@ typedef enum {
     SKG_ERR_NOT_WARMED = 4,  /* the stream is capturing a graph and its split-K
                                 workspace is too small: warm up first */
     SKG_ERR_HIP = 5,         /* a HIP runtime call or a kernel launch failed */
-    SKG_ERR_NO_DEVICE = 6    /* no gfx950 device / the code object does not load */
+    SKG_ERR_NO_DEVICE = 6,   /* no gfx950 device / the code object does not load */
+    SKG_ERR_SCRATCH_TOO_SMALL = 7 /* skinny_gemm_bf16_noalloc only: the shape's
+                                     split-K configuration needs more than the
+                                     static scratch holds; use skinny_gemm_bf16 */
 } skg_status;
 
 typedef enum { SKG_OUT_F32 = 0, SKG_OUT_BF16 = 1 } skg_out_dtype;
@@ -125,6 +129,10 @@ typedef enum {
 
 #define SKG_MAX_M 64      /* the matrix-core kinds; the VALU kinds take M <= 16 */
 #define SKG_MAX_M_VALU 16
+/* Static scratch of skinny_gemm_bf16_noalloc, per GPU: arrival counters
+ * (32-bit words) and fp32 split-K partials. */
+#define SKG_SCRATCH_TICKETS 4096
+#define SKG_SCRATCH_PARTIAL_BYTES (1 << 20)
 
 /* A kernel configuration: what skinny_gemm_dispatch returns and what
  * skinny_gemm_bf16_with_config accepts.  Plain data; compare field by field. */
@@ -173,6 +181,36 @@ int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
 int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, int K,
                            int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
                            void *stream, void *start_event, void *stop_event);
+
+/*
+ * Same as skinny_gemm_bf16 (same arguments, configuration, kernels and bits),
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture without a prior warm-up, tight serving loops, harnesses that forbid
+ * allocation.  It calls no hipMalloc, hipFree or other allocating routine.
+ * The split-K workspace is one statically sized array per GPU in the
+ * library's code object, not a per-stream buffer:
+ *   - SKG_SCRATCH_TICKETS arrival counters and SKG_SCRATCH_PARTIAL_BYTES of
+ *     fp32 partials (about 1 MiB per GPU the library runs on, held until the
+ *     process ends).  That covers every configuration dispatch returns for
+ *     M <= 16 (the largest needs 98 KB) and the middle tier except its
+ *     two-pass configurations on wide N (e.g. M > 32 at K = 7168, N = 2112).
+ *     A shape whose configuration needs more returns
+ *     SKG_ERR_SCRATCH_TOO_SMALL before any GPU work.
+ *   - Every call on one GPU shares that GPU's array.  Calls that overlap in
+ *     time on one GPU (on different streams, or a graph replayed beside
+ *     them) RACE on it and may return wrong results: serialise them, e.g. on
+ *     one stream.  Calls whose configuration has no K split (most large
+ *     shapes) do not touch the array.
+ *   - The counters must be zero when a call starts: they start at zero, the
+ *     first call on a device clears them in stream order (a kernel, not a
+ *     memset), and every call that completes leaves them at zero.
+ *   - The first call on a device looks up the array's address (per device,
+ *     with that device current); skinny_gemm_warmup does the same lookup, so
+ *     calling it beforehand keeps that step out of a later capture.
+ */
+int skinny_gemm_bf16_noalloc(const void *A, const void *B, void *C, int M, int N, int K,
+                             int64_t lda, int64_t ldb, int64_t ldc, int out_dtype,
+                             void *stream);
 
 /* Same as skinny_gemm_bf16 with an explicit configuration (tests, tuning).
  * An invalid or unsupported configuration returns SKG_ERR_INVALID_ARG. */

@@ -19,6 +19,7 @@ SKG_ERR_MISALIGNED = 3
 SKG_ERR_NOT_WARMED = 4
 SKG_ERR_HIP = 5
 SKG_ERR_NO_DEVICE = 6
+SKG_ERR_SCRATCH_TOO_SMALL = 7
 
 SKG_OUT_F32 = 0
 SKG_OUT_BF16 = 1
@@ -35,6 +36,8 @@ SKG_INNER_MFMA_RING = 4
 SKG_INNER_MFMA_RING_GA = 5
 SKG_MAX_M = 64
 SKG_MAX_M_VALU = 16
+SKG_SCRATCH_TICKETS = 4096
+SKG_SCRATCH_PARTIAL_BYTES = 1 << 20
 
 # Compiled (row_tiles, depth) pairs per inner product (the library's tables).
 VALU_VARIANTS = ((1, 4), (1, 8), (1, 12), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4))
@@ -85,6 +88,7 @@ _cfgp = ctypes.POINTER(SkgConfig)
 
 SIGNATURES = {
     "skinny_gemm_bf16": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp]),
+    "skinny_gemm_bf16_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp]),
     "skinny_gemm_bf16_timed": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i, _vp,
                                     _vp, _vp]),
     "skinny_gemm_bf16_with_config": (_i, [_vp, _vp, _vp, _i, _i, _i, _i64, _i64, _i64, _i,

@@ -228,9 +228,24 @@ int check_args(const void *A, const void *B, const void *C, int M, int N, int K,
     return SKG_OK;
 }
 
+// Whether cfg's split-K workspace for (M, K, N) fits the static scratch: its
+// counters in the first kScratchTicketWords words, its partials in the
+// kScratchPartialFloats words after them (true without a K split).
+bool fits_static_scratch(int M, int K, int N, const skg_config &cfg) {
+    if (K < kChunk || cfg.split_k <= 1) return true;  // no workspace
+    Geometry g;
+    if (!make_geometry(M, K, N, cfg, &g)) return false;
+    return g.n_tickets <= (size_t)kScratchTicketWords &&
+           g.ws_floats <= (size_t)kScratchPartialFloats;
+}
+
+// static_ws: the split-K workspace is the per-device static scratch (the
+// no-allocation entry point; the caller has checked that it fits) instead
+// of the stream's allocated workspace.
 int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda, int64_t ldb,
         int64_t ldc, int out_dtype, void *stream_v, const skg_config &cfg,
-        void *start_v = nullptr, void *stop_v = nullptr, bool f32w = false) {
+        void *start_v = nullptr, void *stop_v = nullptr, bool f32w = false,
+        bool static_ws = false) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     hipEvent_t start = reinterpret_cast<hipEvent_t>(start_v);
     hipEvent_t stop = reinterpret_cast<hipEvent_t>(stop_v);
@@ -272,7 +287,12 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.stash_offset = g.stash_offset;
     p.flag_offset = g.flag_offset;
     p.tr_offset = g.tr_offset;
-    if (cfg.split_k > 1) {
+    if (cfg.split_k > 1 && static_ws) {
+        void *base = nullptr;
+        if (const hipError_t e = static_scratch(stream, &base)) return hip_status(e);
+        p.tickets = reinterpret_cast<unsigned *>(base);
+        p.ws = reinterpret_cast<float *>(base) + kScratchTicketWords;
+    } else if (cfg.split_k > 1) {
         Workspace w;
         const int st = get_workspace(stream, g.ws_floats, g.n_tickets, &w);
         if (st != SKG_OK) return st;
@@ -498,6 +518,13 @@ int warmup_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_value
             }
         }
     }
+    // the no-allocation entry point's scratch address on this device (a
+    // lookup and a counter clear, no allocation), so that its first call
+    // needs neither
+    {
+        void *base = nullptr;
+        if (const hipError_t e = static_scratch(stream, &base)) return hip_status(e);
+    }
     int nd = 0;
     {
         std::vector<skg_config> uniq;
@@ -578,6 +605,19 @@ int skinny_gemm_bf16(const void *A, const void *B, void *C, int M, int N, int K,
     if (ds != SKG_OK) return ds;
     log_choice(false, M, K, N, cfg);
     return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg);
+}
+
+int skinny_gemm_bf16_noalloc(const void *A, const void *B, void *C, int M, int N, int K,
+                             int64_t lda, int64_t ldb, int64_t ldc, int out_dtype, void *stream) {
+    const int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, out_dtype);
+    if (st != SKG_OK || M == 0 || N == 0) return st;
+    skg_config cfg;
+    const int ds = skinny_gemm_dispatch(M, K, N, &cfg);
+    if (ds != SKG_OK) return ds;
+    if (!fits_static_scratch(M, K, N, cfg)) return SKG_ERR_SCRATCH_TOO_SMALL;
+    log_choice(false, M, K, N, cfg);
+    return run(A, B, C, M, N, K, lda, ldb, ldc, out_dtype, stream, cfg, nullptr, nullptr, false,
+               true);
 }
 
 int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, int K,
@@ -704,6 +744,9 @@ const char *skinny_gemm_strerror(int status) {
             return "stream is capturing and its split-K workspace is too small: warm up first";
         case SKG_ERR_HIP: return "HIP runtime error";
         case SKG_ERR_NO_DEVICE: return "no gfx950 device";
+        case SKG_ERR_SCRATCH_TOO_SMALL:
+            return "the split-K workspace of this shape exceeds the static scratch of "
+                   "skinny_gemm_bf16_noalloc: use skinny_gemm_bf16";
         default: return "unknown status";
     }
 }

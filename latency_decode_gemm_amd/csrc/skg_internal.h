@@ -99,6 +99,16 @@ hipError_t launch_stream_read(const void *src, size_t n16, void *sink, hipStream
 // Loads a kernel's code object (forces lazy loading) for availability checks.
 hipError_t probe_kernels();
 
+// Static split-K scratch of the no-allocation entry point (skg_scratch.hip):
+// kScratchTicketWords arrival counters, then kScratchPartialFloats fp32
+// partials, one array per device.
+constexpr int kScratchTicketWords = SKG_SCRATCH_TICKETS;
+constexpr int kScratchPartialFloats = SKG_SCRATCH_PARTIAL_BYTES / 4;
+constexpr int kScratchWords = kScratchTicketWords + kScratchPartialFloats;
+// This device's scratch address (looked up once per device, with the device
+// current; the counters are cleared on `stream` at that first use).
+hipError_t static_scratch(hipStream_t stream, void **ptr);
+
 // MFMA transpose tile per wave and 16-row tile: 16 rows x 16 chunks x 16 B.
 constexpr int kTileBytes = 4096;
 

@@ -83,6 +83,21 @@ def skinny_gemm_bf16(A, B, out=None, out_dtype=None, stream=None):
     return out
 
 
+def skinny_gemm_bf16_noalloc(A, B, out, stream=None):
+    """As :func:`skinny_gemm_bf16`, allocating nothing: ``out`` must be given,
+    and the split-K workspace is the library's static per-GPU scratch (calls
+    that overlap on one GPU race on it).  Raises SkinnyGemmError with
+    SKG_ERR_SCRATCH_TOO_SMALL when the shape's workspace does not fit."""
+    if out is None:
+        raise ValueError("skinny_gemm_bf16_noalloc needs `out` (it allocates nothing)")
+    M, N, K, lda, ldb, ldc, odt, out = _marshal(A, B, out, None)
+    st = _capi.lib().skinny_gemm_bf16_noalloc(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N,
+                                              K, lda, ldb, ldc, odt,
+                                              _stream_handle(stream, A.device))
+    check(st, "skinny_gemm_bf16_noalloc")
+    return out
+
+
 def skinny_gemm_bf16_timed(A, B, start_event, stop_event, out=None, out_dtype=None, stream=None):
     """As :func:`skinny_gemm_bf16`; the kernel's own start and end are
     recorded in ``start_event`` / ``stop_event`` (:class:`HipEvent` or raw

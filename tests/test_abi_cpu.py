@@ -44,7 +44,7 @@ def test_struct_layout_matches_header():
 
 
 def test_strerror_covers_codes():
-    for code in range(7):
+    for code in range(8):
         assert skg.skinny_gemm_strerror(code) != "unknown status"
     assert skg.skinny_gemm_strerror(99) == "unknown status"
 
@@ -525,3 +525,35 @@ def test_hip_errors_are_recorded_on_the_workspace_path():
         st, err = got[what]
         assert st == skg.SKG_ERR_HIP, (what, got)
         assert err != 0, (what, got)
+
+
+def _noalloc(A=FAKE, B=FAKE, C=FAKE, M=4, N=256, K=7168, lda=7168, ldb=7168, ldc=256, odt=0):
+    return _capi.lib().skinny_gemm_bf16_noalloc(A, B, C, M, N, K, lda, ldb, ldc, odt, None)
+
+
+def test_noalloc_checks_arguments_like_the_allocating_entry():
+    """The same argument checks as skinny_gemm_bf16, before any HIP call."""
+    for kw, code in [(dict(M=-1), skg.SKG_ERR_INVALID_ARG), (dict(M=65), skg.SKG_ERR_UNSUPPORTED),
+                     (dict(ldc=255), skg.SKG_ERR_INVALID_ARG), (dict(C=0), skg.SKG_ERR_INVALID_ARG),
+                     (dict(A=FAKE + 8), skg.SKG_ERR_MISALIGNED), (dict(odt=2), skg.SKG_ERR_INVALID_ARG),
+                     (dict(M=0), skg.SKG_OK), (dict(N=0, A=0, B=0, C=0), skg.SKG_OK)]:
+        assert _noalloc(**kw) == code, kw
+        assert _call(**kw) == code, kw
+
+
+def test_noalloc_scratch_covers_the_skinny_tier_and_rejects_larger_workspaces():
+    """Every configuration dispatch returns for M <= 16 on the workload shapes
+    fits the static scratch; a shape whose split-K workspace does not (the
+    two-pass split of M = 48 at K = 7168, N = 2112) is rejected with
+    SKG_ERR_SCRATCH_TOO_SMALL before any GPU work (placeholder pointers)."""
+    cap = skg.SKG_SCRATCH_PARTIAL_BYTES + 4 * skg.SKG_SCRATCH_TICKETS
+    for (K, N) in ((7168, 256), (7168, 384), (2880, 128), (7168, 2112), (1536, 24576),
+                   (14336, 7168)):
+        for M in range(1, 17):
+            cfg = skg.skinny_gemm_dispatch(M, K, N)
+            assert skg.skinny_gemm_workspace_bytes(M, K, N, cfg) <= cap // 8, (M, K, N)
+    M, K, N = 48, 7168, 2112
+    cfg = skg.skinny_gemm_dispatch(M, K, N)
+    assert skg.skinny_gemm_workspace_bytes(M, K, N, cfg) > skg.SKG_SCRATCH_PARTIAL_BYTES
+    assert _noalloc(M=M, K=K, N=N, lda=K, ldb=K, ldc=N) == skg.SKG_ERR_SCRATCH_TOO_SMALL
+    assert "static scratch" in skg.skinny_gemm_strerror(skg.SKG_ERR_SCRATCH_TOO_SMALL)
