@@ -72,10 +72,11 @@ def structures(skg, M, K, N, inner_set, check=None):
                                                      depth=d, rb_per_wg=rpw)
                             if check(M, K, N, cfg):
                                 out.append(cfg)
-                # rows dealt evenly to 256 or 512 workgroups (backend 3), as
-                # row blocks x K slices, when the waves cover a block with
-                # little to spare
-                for per_cu in (1, 2):
+                # rows dealt evenly to 256, 512, 1024 or 2048 workgroups
+                # (backend 3), as row blocks x K slices, when the waves cover
+                # a block with little to spare (several workgroups per CU
+                # give more waves, each with a shorter ring)
+                for per_cu in (1, 2, 4, 8):
                     for S in (1, 2, 4, 8):
                         need = math.ceil(N / min(N, 256 * per_cu // S))
                         if not need <= nb < 2 * need + 16:
