@@ -88,8 +88,12 @@ typedef enum { SKG_OUT_F32 = 0, SKG_OUT_BF16 = 1 } skg_out_dtype;
 typedef enum {
     SKG_BACKEND_DOT = 0,   /* each workgroup covers all of K for its blocks of rows of B */
     SKG_BACKEND_SPLITK = 1, /* split_k workgroups per row block, each one slice of K;
-                               fp32 partials are summed in a fixed order by the
-                               last workgroup to finish (no spin-wait) */
+                               the slices' fp32 partials of each output are
+                               added pairwise along a fixed binary tree, each
+                               value carried by an atomic exchange on the
+                               tree node's slot (no fence, no spin-wait); the
+                               order of the additions is the tree's, whatever
+                               the order in which workgroups finish */
     SKG_BACKEND_SPLITK_2PASS = 2, /* as SPLITK, but a second kernel on the same
                                      stream sums the partials in split order */
     SKG_BACKEND_EVEN = 3 /* 256 * rb_per_wg workgroups (256 CUs: rb_per_wg
@@ -129,9 +133,9 @@ typedef enum {
 
 #define SKG_MAX_M 64      /* the matrix-core kinds; the VALU kinds take M <= 16 */
 #define SKG_MAX_M_VALU 16
-/* Static scratch of skinny_gemm_bf16_noalloc, per GPU: arrival counters
- * (32-bit words) and fp32 split-K partials. */
-#define SKG_SCRATCH_TICKETS 4096
+/* Static scratch of skinny_gemm_bf16_noalloc, per GPU: the one-pass split-K
+ * tree slots and the two-pass split-K fp32 partials. */
+#define SKG_SCRATCH_SLOT_BYTES (1 << 20)
 #define SKG_SCRATCH_PARTIAL_BYTES (1 << 20)
 
 /* A kernel configuration: what skinny_gemm_dispatch returns and what
@@ -189,19 +193,20 @@ int skinny_gemm_bf16_timed(const void *A, const void *B, void *C, int M, int N, 
  * allocation.  It calls no hipMalloc, hipFree or other allocating routine.
  * The split-K workspace is one statically sized array per GPU in the
  * library's code object, not a per-stream buffer:
- *   - SKG_SCRATCH_TICKETS arrival counters and SKG_SCRATCH_PARTIAL_BYTES of
- *     fp32 partials (about 1 MiB per GPU the library runs on, held until the
- *     process ends).  That covers every configuration dispatch returns for
- *     M <= 16 (the largest needs 98 KB) and the middle tier except its
- *     two-pass configurations on wide N (e.g. M > 32 at K = 7168, N = 2112).
- *     A shape whose configuration needs more returns
- *     SKG_ERR_SCRATCH_TOO_SMALL before any GPU work.
+ *   - SKG_SCRATCH_SLOT_BYTES of one-pass split-K tree slots and
+ *     SKG_SCRATCH_PARTIAL_BYTES of two-pass fp32 partials (2 MiB per GPU the
+ *     library runs on, held until the process ends).  That covers every
+ *     configuration dispatch returns for M <= 16 (the largest needs
+ *     144 KB) and the middle tier except its two-pass configurations on
+ *     wide N (e.g. M > 32 at K = 7168, N = 2112).  A shape whose
+ *     configuration needs more returns SKG_ERR_SCRATCH_TOO_SMALL before any
+ *     GPU work.
  *   - Every call on one GPU shares that GPU's array.  Calls that overlap in
  *     time on one GPU (on different streams, or a graph replayed beside
  *     them) RACE on it and may return wrong results: serialise them, e.g. on
  *     one stream.  Calls whose configuration has no K split (most large
  *     shapes) do not touch the array.
- *   - The counters must be zero when a call starts: they start at zero, the
+ *   - The slots must be zero when a call starts: they start at zero, the
  *     first call on a device clears them in stream order (a kernel, not a
  *     memset), and every call that completes leaves them at zero.
  *   - The first call on a device looks up the array's address (per device,
@@ -230,9 +235,11 @@ int skinny_gemm_dispatch(int M, int K, int N, skg_config *out);
 /* Whether cfg can run (M, K, N): SKG_OK or SKG_ERR_INVALID_ARG.  Pure host. */
 int skinny_gemm_check_config(int M, int K, int N, const skg_config *cfg);
 
-/* Bytes of split-K workspace (partials, plus tickets for the single-pass
- * sum of SKG_BACKEND_SPLITK and of SKG_BACKEND_EVEN with split_k >= 2) cfg
- * needs for (M, K, N); 0 without a K split.  Pure host. */
+/* Bytes of split-K workspace cfg needs for (M, K, N): the tree slots of the
+ * one-pass split (SKG_BACKEND_SPLITK, and SKG_BACKEND_EVEN with split_k >= 2:
+ * 8 bytes per output and tree node, split_k - 1 nodes) or the partials of the
+ * two-pass split (4 bytes per output and slice); 0 without a K split.  Pure
+ * host. */
 int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg,
                                 size_t *bytes);
 

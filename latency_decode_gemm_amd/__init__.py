@@ -10,7 +10,7 @@ from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_EVEN, SKG_BACKEND_SPLITK, SKG_B
                     SKG_ERR_UNSUPPORTED, SKG_INNER_MFMA, SKG_INNER_MFMA_GA,
                     SKG_INNER_MFMA_RING, SKG_INNER_MFMA_RING_GA, SKG_INNER_VALU,
                     SKG_INNER_VALU_GA, SKG_MAX_M, SKG_MAX_M_VALU, SKG_OK,
-                    SKG_OUT_BF16, SKG_OUT_F32, SKG_SCRATCH_PARTIAL_BYTES, SKG_SCRATCH_TICKETS,
+                    SKG_OUT_BF16, SKG_OUT_F32, SKG_SCRATCH_PARTIAL_BYTES, SKG_SCRATCH_SLOT_BYTES,
                     HipEvent, SkgConfig, SkinnyGemmError)
 from .ops import (skinny_gemm_available, skinny_gemm_bf16, skinny_gemm_bf16_noalloc,
                   skinny_gemm_bf16_timed,

@@ -36,7 +36,7 @@ SKG_INNER_MFMA_RING = 4
 SKG_INNER_MFMA_RING_GA = 5
 SKG_MAX_M = 64
 SKG_MAX_M_VALU = 16
-SKG_SCRATCH_TICKETS = 4096
+SKG_SCRATCH_SLOT_BYTES = 1 << 20
 SKG_SCRATCH_PARTIAL_BYTES = 1 << 20
 
 # Compiled (row_tiles, depth) pairs per inner product (the library's tables).

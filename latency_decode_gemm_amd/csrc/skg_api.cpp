@@ -153,10 +153,10 @@ int hip_status(hipError_t e) {
 }
 
 struct Workspace {
-    float *ws = nullptr;
+    float *ws = nullptr;  // two-pass partials
     size_t ws_floats = 0;
-    unsigned *tickets = nullptr;
-    size_t n_tickets = 0;
+    unsigned long long *slots = nullptr;  // one-pass tree slots, zero between calls
+    size_t slot_words = 0;                // (32-bit words)
 };
 
 std::mutex g_ws_mu;
@@ -167,15 +167,15 @@ std::map<std::pair<int, void *>, Workspace> g_ws;
 // has been replaced is never freed: a graph captured earlier on this stream
 // holds its addresses in its kernel arguments and may be replayed at any time,
 // so every buffer stays allocated until the process ends (the sizes only grow,
-// so at most a few buffers per stream are ever retired).  The new tickets are
+// so at most a few buffers per stream are ever retired).  The new slots are
 // zeroed in stream order before the first kernel that uses them; no host or
 // device synchronisation is needed, since no buffer is freed.
-int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, Workspace *out) {
+int get_workspace(hipStream_t stream, size_t need_floats, size_t need_words, Workspace *out) {
     int dev = 0;
     if (const hipError_t e = hipGetDevice(&dev)) return hip_status(e);
     std::lock_guard<std::mutex> lock(g_ws_mu);
     Workspace &w = g_ws[std::make_pair(dev, (void *)stream)];
-    if (w.ws_floats >= need_floats && w.n_tickets >= need_tickets) {
+    if (w.ws_floats >= need_floats && w.slot_words >= need_words) {
         *out = w;
         return SKG_OK;
     }
@@ -183,26 +183,26 @@ int get_workspace(hipStream_t stream, size_t need_floats, size_t need_tickets, W
     if (const hipError_t e = hipStreamIsCapturing(stream, &cap)) return hip_status(e);
     if (cap != hipStreamCaptureStatusNone) return SKG_ERR_NOT_WARMED;
     const size_t nf = std::max(need_floats, w.ws_floats);
-    const size_t nt = std::max(need_tickets, w.n_tickets);
+    const size_t nw = (std::max(need_words, w.slot_words) + 1) / 2 * 2;  // whole 64-bit slots
     float *ws = nullptr;
-    unsigned *tk = nullptr;
+    unsigned long long *sl = nullptr;
     if (const hipError_t e = hipMalloc(&ws, std::max<size_t>(nf, 1) * sizeof(float)))
         return hip_status(e);
-    if (const hipError_t e = hipMalloc(&tk, std::max<size_t>(nt, 1) * sizeof(unsigned))) {
+    if (const hipError_t e = hipMalloc(&sl, std::max<size_t>(nw, 2) * sizeof(unsigned))) {
         (void)hipFree(ws);
         return hip_status(e);
     }
     // (the stream is not capturing here, so this memset is never part of a graph)
     if (const hipError_t e =
-            hipMemsetAsync(tk, 0, std::max<size_t>(nt, 1) * sizeof(unsigned), stream)) {
+            hipMemsetAsync(sl, 0, std::max<size_t>(nw, 2) * sizeof(unsigned), stream)) {
         (void)hipFree(ws);
-        (void)hipFree(tk);
+        (void)hipFree(sl);
         return hip_status(e);
     }
     w.ws = ws;
     w.ws_floats = nf;
-    w.tickets = tk;
-    w.n_tickets = nt;
+    w.slots = sl;
+    w.slot_words = nw;
     *out = w;
     return SKG_OK;
 }
@@ -229,13 +229,13 @@ int check_args(const void *A, const void *B, const void *C, int M, int N, int K,
 }
 
 // Whether cfg's split-K workspace for (M, K, N) fits the static scratch: its
-// counters in the first kScratchTicketWords words, its partials in the
+// tree slots in the first kScratchSlotWords words, its partials in the
 // kScratchPartialFloats words after them (true without a K split).
 bool fits_static_scratch(int M, int K, int N, const skg_config &cfg) {
     if (K < kChunk || cfg.split_k <= 1) return true;  // no workspace
     Geometry g;
     if (!make_geometry(M, K, N, cfg, &g)) return false;
-    return g.n_tickets <= (size_t)kScratchTicketWords &&
+    return g.slot_words <= (size_t)kScratchSlotWords &&
            g.ws_floats <= (size_t)kScratchPartialFloats;
 }
 
@@ -285,19 +285,18 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.num_rb = g.num_rb;
     p.lds_stride = g.lds_stride;
     p.stash_offset = g.stash_offset;
-    p.flag_offset = g.flag_offset;
     p.tr_offset = g.tr_offset;
     if (cfg.split_k > 1 && static_ws) {
         void *base = nullptr;
         if (const hipError_t e = static_scratch(stream, &base)) return hip_status(e);
-        p.tickets = reinterpret_cast<unsigned *>(base);
-        p.ws = reinterpret_cast<float *>(base) + kScratchTicketWords;
+        p.slots = reinterpret_cast<unsigned long long *>(base);
+        p.ws = reinterpret_cast<float *>(base) + kScratchSlotWords;
     } else if (cfg.split_k > 1) {
         Workspace w;
-        const int st = get_workspace(stream, g.ws_floats, g.n_tickets, &w);
+        const int st = get_workspace(stream, g.ws_floats, g.slot_words, &w);
         if (st != SKG_OK) return st;
         p.ws = w.ws;
-        p.tickets = w.tickets;
+        p.slots = w.slots;
     }
     return hip_status(launch(p, g, cfg, stream, start, stop));
 }
@@ -378,18 +377,18 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     const size_t per_block = valu ? (size_t)M * r.rows_per_wg : (size_t)16 * mt * r.rows_per_wg;
     const size_t blocks_per_wg = (size_t)ceil_div(r.num_rb, r.grid_rb);
     // (a row block covered by one wave is written from registers)
-    // (the single-pass split-K settles row blocks workgroup by workgroup)
+    // (the single-pass split-K combines each output through the stash)
     const bool one_pass = cfg.split_k > 1 && cfg.backend != SKG_BACKEND_SPLITK_2PASS;
     const bool direct = cfg.waves_k == 1 && !one_pass;
     const size_t stash_bytes =
         direct ? 0 : blocks_per_wg * cfg.waves_k * per_block * sizeof(float);
-    if (r.stash_offset + stash_bytes > (size_t)kMaxLdsBytes) return false;
-    r.flag_offset = (int)(r.stash_offset + stash_bytes);
-    r.lds_bytes = r.flag_offset + 16;
+    r.lds_bytes = r.stash_offset + stash_bytes;
     if (r.lds_bytes > (size_t)kMaxLdsBytes) return false;
     r.threads = 64 * cfg.waves_n * cfg.waves_k;
-    r.ws_floats = (S > 1) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
-    r.n_tickets = one_pass ? (size_t)r.num_rb : 0;
+    // two-pass: every slice's partials; one pass: split_k - 1 tree nodes of
+    // one 64-bit slot per output
+    r.ws_floats = (S > 1 && !one_pass) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
+    r.slot_words = one_pass ? (size_t)r.num_rb * (S - 1) * M * r.rows_per_wg * 2 : 0;
     if ((int64_t)r.grid_rb * S > 0x7FFFFFFF) return false;
     *g = r;
     return true;
@@ -503,7 +502,7 @@ int warmup_impl(bool f32w, const int *kn_pairs, int n_shapes, const int *m_value
             Geometry g;
             if (!make_geometry(M, K, N, c, &g)) return SKG_ERR_INVALID_ARG;
             need_f = std::max(need_f, g.ws_floats);
-            need_t = std::max(need_t, g.n_tickets);
+            need_t = std::max(need_t, g.slot_words);
             bool seen = false;
             for (auto &t : todo)
                 seen = seen || (config_equal(t.first, c) && t.second.first == M &&
@@ -592,7 +591,7 @@ int skinny_gemm_workspace_bytes(int M, int K, int N, const skg_config *cfg, size
     if (!cfg || !bytes) return SKG_ERR_INVALID_ARG;
     Geometry g;
     if (!make_geometry(M, K, N, *cfg, &g)) return SKG_ERR_INVALID_ARG;
-    *bytes = g.ws_floats * sizeof(float) + g.n_tickets * sizeof(unsigned);
+    *bytes = g.ws_floats * sizeof(float) + g.slot_words * sizeof(unsigned);
     return SKG_OK;
 }
 

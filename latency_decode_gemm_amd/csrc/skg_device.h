@@ -33,13 +33,13 @@
 //    remains.
 //  * Cross-wave (waves_k > 1): partials go through LDS (double-buffered per
 //    row block) and wave 0 adds them in wave order.  Cross-workgroup
-//    (split_k > 1): each workgroup stores its fp32 partial tile with
-//    agent-scope atomic stores and takes a ticket with one agent-scope
-//    release add (one per workgroup, after a workgroup barrier); the
-//    workgroup that draws the last ticket performs an agent-scope acquire,
-//    reads the split_k partials, adds them in split order, writes C and
-//    resets the ticket.  Nothing waits for another workgroup, and no
-//    summation order depends on timing, so results are bit-reproducible.
+//    (split_k > 1, one pass): the split_k partials of each output are
+//    combined pairwise along a fixed binary tree, the value itself carried by
+//    a 64-bit atomic exchange on the tree node's slot; whichever workgroup
+//    arrives second at a node adds left + right and climbs, and the one that
+//    completes the root writes C.  Nothing waits for another workgroup, and
+//    the summation order is the tree's whatever the arrival order, so results
+//    are bit-reproducible.
 //  * Epilogue: fp32 stores, or bf16 round-to-nearest-even, at C[m*ldc + n];
 //    other bytes of C are never written.
 #pragma once
@@ -315,12 +315,12 @@ struct Pow2Ceil {
 };
 
 // ---- split-K ------------------------------------------------------------------
-__device__ __forceinline__ void ws_store(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float ws_load(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Slot word of a tree node: the fp32 bits of a partial sum in the upper half,
+// the side it came from (0 left, 1 right) in bit 1, and bit 0 set, so an
+// empty slot (0) differs from every partial, -0.0 and NaN included.
+__device__ __forceinline__ unsigned long long slot_word(float v, int side) {
+    return ((unsigned long long)__builtin_bit_cast(uint32_t, v) << 32) |
+           ((unsigned long long)side << 1) | 1ull;
 }
 
 // Rows of row block rb: [start, start + count).  Uniform blocks of
@@ -337,52 +337,41 @@ __device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start,
     }
 }
 
-// Workgroup barrier with release/acquire fences over every address space, so
-// that each thread's earlier global stores happen before whatever any thread
-// of the workgroup does after it.
-__device__ __forceinline__ void wg_barrier_all() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Called by every thread of the workgroup once its partials of row block rb
-// are stored (ws_store).  The ordering is the language's, not the hardware's:
-// the workgroup barrier orders every thread's partial stores before thread 0's
-// ticket, which is an agent-scope release (it publishes them to the other
-// workgroups); the workgroup that draws the last ticket performs an
-// agent-scope acquire fence before the barrier that lets its threads read the
-// partials, so every other workgroup's release happens before those reads.
-// Only the last arriver pays for the acquire.  That workgroup adds the split_k
-// partials ws[rb][0..S)[m][rl] in split order and writes C.
-__device__ __forceinline__ void splitk_complete(const KParams &p, int rb, unsigned *flag) {
-    wg_barrier_all();
-    if (threadIdx.x == 0) {
-        const unsigned t = __hip_atomic_fetch_add(&p.tickets[rb], 1u, __ATOMIC_RELEASE,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = t == (unsigned)(p.split_k - 1);
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        *flag = last ? 1u : 0u;
-    }
-    wg_barrier_all();
-    if (*flag) {
-        const int NB = p.rows_per_wg;
-        const int total = p.M * NB;
-        const float *base = p.ws + (size_t)rb * p.split_k * total;
-        int bst, bcnt;
-        block_rows(p, rb, bst, bcnt);
-        for (int i = threadIdx.x; i < total; i += blockDim.x) {
-            const int m = i / NB;
-            const int rl = i - m * NB;
-            if (rl < bcnt) {
-                float v = 0.0f;
-                for (int s = 0; s < p.split_k; ++s) v += ws_load(base + (size_t)s * total + i);
-                store_c(p, m, bst + rl, v);
-            }
+// Combines this workgroup's partial v of output (m, local row rl) of row block
+// rb, K slice sidx, with the other slices' partials.  The split_k slices are
+// the leaves of a binary tree: at each level, entries 2j and 2j + 1 meet at
+// node j (an odd last entry passes up unchanged), and the node's slot
+// (p.slots, [row block][node][m][local row], zero between calls) takes
+// exactly two exchanges per call.  The first to exchange finds the slot
+// empty and stops; the second finds its sibling's partial, forms left + right
+// (a fixed order, whichever arrived first), empties the slot for the next
+// call and carries the sum one level up.  Returns true in the thread that
+// completes the root, with the full sum in v.  The partials travel inside the
+// atomic operations on one location each: the second exchange reads the first
+// by the atomicity of read-modify-write, so no fence and no other memory is
+// involved (relaxed, agent scope).
+__device__ __forceinline__ bool splitk_combine(const KParams &p, int rb, int sidx, int m, int rl,
+                                               float &v) {
+    const int S = p.split_k;
+    int idx = sidx, width = S, node0 = 0;  // node0: first node of this level
+    while (width > 1) {
+        const int pairs = width >> 1;
+        if (idx < 2 * pairs) {
+            const int side = idx & 1;
+            unsigned long long *slot =
+                p.slots + (((size_t)rb * (S - 1) + node0 + (idx >> 1)) * p.M + m) * p.rows_per_wg + rl;
+            const unsigned long long old = __hip_atomic_exchange(
+                slot, slot_word(v, side), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == 0ull) return false;
+            const float other = __builtin_bit_cast(float, (uint32_t)(old >> 32));
+            v = side ? other + v : v + other;
+            __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&p.tickets[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        node0 += pairs;
+        idx >>= 1;
+        width = (width + 1) >> 1;
     }
+    return true;
 }
 
 // Work assignment of one workgroup.
@@ -408,21 +397,21 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
 // ---- epilogue ------------------------------------------------------------------
 // A row block whose K range is covered by one wave is written straight from
 // that wave's registers.  Otherwise (waves_k > 1, or the single-pass split-K
-// backend, which settles row blocks workgroup by workgroup) each wave parks
-// its partial sums of each row block in LDS (the stash), and after the stream
-// the workgroup's threads take (token, local row) pairs, consecutive threads
-// consecutive rows, add the waves_k partials in wave order, and write C
-// (split_k == 1) or the split's partial (split_k > 1; the single-pass backend
-// then settles the row block with splitk_complete).  base(b, q, rl) is the
-// stash index of token 0 of (row block b, K-wave q, local row rl); mofs(m)
-// adds token m.
+// backend, which combines per output) each wave parks its partial sums of
+// each row block in LDS (the stash), and after the stream the workgroup's
+// threads take (token, local row) pairs, consecutive threads consecutive
+// rows, add the waves_k partials in wave order, and write C (split_k == 1),
+// the split's partial (two-pass), or combine it with the other slices'
+// (splitk_combine; the thread that completes the sum writes C).
+// base(b, q, rl) is the stash index of token 0 of (row block b, K-wave q,
+// local row rl); mofs(m) adds token m.
 __device__ __forceinline__ bool direct_write(const KParams &p) {
     return p.waves_k == 1 && (p.split_k == 1 || p.two_pass);
 }
 
 template <class BASE, class MOFS>
 __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, const float *stash,
-                                             unsigned *flag, BASE base, MOFS mofs) {
+                                             BASE base, MOFS mofs) {
     __syncthreads();
     const int NB = p.rows_per_wg;  // never more than the workgroup's threads
     const int M = p.M;
@@ -434,20 +423,17 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
         const int rb = w.rb0 + b * w.rbs;
         int bst, bcnt;
         block_rows(p, rb, bst, bcnt);
-        float *part = (p.split_k > 1) ? p.ws + (size_t)(rb * p.split_k + w.s) * M * NB + rl
-                                      : nullptr;
         for (int m = m0; m < M; m += mstep) {
             float v = stash[base(b, 0, rl) + mofs(m)];
             for (int q = 1; q < p.waves_k; ++q) v += stash[base(b, q, rl) + mofs(m)];
             if (p.split_k == 1) {
                 if (rl < bcnt) store_c(p, m, bst + rl, v);
             } else if (p.two_pass) {
-                part[m * NB] = v;
-            } else {
-                ws_store(part + m * NB, v);
+                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = v;
+            } else if (rl < bcnt) {
+                if (splitk_combine(p, rb, w.s, m, rl, v)) store_c(p, m, bst + rl, v);
             }
         }
-        if (p.split_k > 1 && !p.two_pass) splitk_complete(p, rb, flag);
     }
 }
 
@@ -492,7 +478,6 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
-    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -654,7 +639,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         if (t0 + i < T) step(buf[i], abuf[i]);
     if (!direct)
         write_blocks(
-            p, w, stash, flag,
+            p, w, stash,
             [&](int b, int q, int rl) { return (b * p.waves_k + q) * M * NB + rl; },
             [&](int m) { return m * NB; });
 }
@@ -718,7 +703,6 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
-    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -910,7 +894,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
     }
     if (!direct)
         write_blocks(
-            p, w, stash, flag,
+            p, w, stash,
             [&](int b, int q, int rl) {
                 const int wq = rl / (16 * G);  // N-wave
                 const int t = (rl >> 4) % G;   // tile
@@ -942,7 +926,6 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
     float *stash = reinterpret_cast<float *>(smem + p.stash_offset);
-    unsigned *flag = reinterpret_cast<unsigned *>(smem + p.flag_offset);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1109,7 +1092,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     wait_vmcnt<0>();
     if (!direct)
         write_blocks(
-            p, w, stash, flag,
+            p, w, stash,
             [&](int b, int q, int rl) {
                 const int wq = rl / (16 * G);  // N-wave
                 const int t = (rl >> 4) % G;   // tile

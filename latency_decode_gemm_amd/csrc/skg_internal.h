@@ -30,8 +30,9 @@ struct KParams {
     const uint16_t *A;
     const uint16_t *B;
     void *C;
-    float *ws;          // split-K partials [num_rb][split_k][M][rows_per_wg]
-    unsigned *tickets;  // split-K arrival counters [num_rb], zero between calls
+    float *ws;                 // two-pass split-K partials [num_rb][split_k][M][rows_per_wg]
+    unsigned long long *slots; // one-pass split-K tree slots [num_rb][split_k - 1][M][rows_per_wg],
+                               // zero between calls
     int64_t lda, ldb, ldc;
     int M, N, K;
     int out_bf16;
@@ -48,7 +49,6 @@ struct KParams {
     int lds_stride;   // bf16 elements per staged A row in LDS
     int stash_offset; // byte offset in LDS of the per-row-block partial sums
                       // that the epilogue combines
-    int flag_offset;  // byte offset of the split-K "last arrival" flag in LDS
     int tr_offset;    // byte offset of the MFMA kernel's per-wave transpose tiles
     int w_f32;        // B holds fp32 weights (rows of ldb fp32 elements)
 };
@@ -63,9 +63,9 @@ struct Geometry {
     int threads;
     int lds_stride;    // elements
     size_t lds_bytes;
-    int stash_offset, flag_offset, tr_offset;
-    size_t ws_floats;  // split-K partial floats
-    size_t n_tickets;
+    int stash_offset, tr_offset;
+    size_t ws_floats;   // two-pass split-K partial floats
+    size_t slot_words;  // one-pass split-K tree slots, in 32-bit words (zero between calls)
 };
 
 // Fills g; returns false if cfg cannot run (M, K, N).
@@ -100,13 +100,13 @@ hipError_t launch_stream_read(const void *src, size_t n16, void *sink, hipStream
 hipError_t probe_kernels();
 
 // Static split-K scratch of the no-allocation entry point (skg_scratch.hip):
-// kScratchTicketWords arrival counters, then kScratchPartialFloats fp32
-// partials, one array per device.
-constexpr int kScratchTicketWords = SKG_SCRATCH_TICKETS;
+// kScratchSlotWords 32-bit words of tree slots (zero between calls), then
+// kScratchPartialFloats fp32 partials, one array per device.
+constexpr int kScratchSlotWords = SKG_SCRATCH_SLOT_BYTES / 4;
 constexpr int kScratchPartialFloats = SKG_SCRATCH_PARTIAL_BYTES / 4;
-constexpr int kScratchWords = kScratchTicketWords + kScratchPartialFloats;
+constexpr int kScratchWords = kScratchSlotWords + kScratchPartialFloats;
 // This device's scratch address (looked up once per device, with the device
-// current; the counters are cleared on `stream` at that first use).
+// current; the slots are cleared on `stream` at that first use).
 hipError_t static_scratch(hipStream_t stream, void **ptr);
 
 // MFMA transpose tile per wave and 16-row tile: 16 rows x 16 chunks x 16 B.

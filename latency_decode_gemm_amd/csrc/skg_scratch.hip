@@ -3,12 +3,13 @@
 // GPU, created when the code object is loaded, instead of a buffer the
 // library allocates per stream.
 //
-// Layout (32-bit words): kScratchTicketWords arrival counters, then the fp32
-// partials.  The counters must be zero when a call starts.  Static storage
-// starts zeroed, the first use on a device clears them once more in stream
-// order, and every call that completes leaves them at zero (the last
-// workgroup of each row block resets its counter), so no call clears them.
-// The partials are written before they are read within each call.
+// Layout (32-bit words): kScratchSlotWords words of one-pass split-K tree
+// slots (64-bit each), then the fp32 partials of the two-pass split.  The
+// slots must be zero when a call starts.  Static storage starts zeroed, the
+// first use on a device clears them once more in stream order, and every call
+// that completes leaves them at zero (the second workgroup at each tree node
+// empties its slot), so no call clears them.  The partials are written before
+// they are read within each call.
 #include <mutex>
 
 #include "skg_internal.h"
@@ -43,8 +44,8 @@ hipError_t static_scratch(hipStream_t stream, void **ptr) {
         if (addr == nullptr) return hipErrorInvalidSymbol;
         // a kernel (not a memset), so that a first call under graph capture
         // records nothing a replay could mishandle
-        hipLaunchKernelGGL(skg_clear_words_kernel, dim3(1), dim3(256), 0, stream,
-                           reinterpret_cast<unsigned *>(addr), kScratchTicketWords);
+        hipLaunchKernelGGL(skg_clear_words_kernel, dim3(256), dim3(256), 0, stream,
+                           reinterpret_cast<unsigned *>(addr), kScratchSlotWords);
         if (const hipError_t e = hipGetLastError()) return e;
         g_addr[dev] = addr;
     }

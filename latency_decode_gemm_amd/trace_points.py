@@ -1,4 +1,5 @@
-"""Per-point kernel times from a rocprofv3 kernel trace of ``bench.py --points-out``.
+"""Per-point kernel times from a rocprofv3 kernel trace of ``bench.py --points-out``,
+or (``--sequence``) of the bench's own timed region.
 
     rocprofv3 --kernel-trace --output-format csv -d OUT -o t -- \\
         python3 bench.py --no-cpu --points-out points.json
@@ -17,6 +18,13 @@ fraction of 8 TB/s, beside the bench's own figures for the point (the
 library GEMM's graph time for the same product among them), taken from
 ``plain.json`` when given: the output of the same command run without the
 profiler, whose event, eager and graph timings the tracing does not inflate.
+
+    rocprofv3 --kernel-trace --output-format csv -d OUT -o t -- python3 bench.py > line.json
+    python -m latency_decode_gemm_amd.trace_points --sequence OUT/.../t_kernel_trace.csv line.json
+
+splits the timed region of a plain bench run (the calls after the two
+marker calls that precede it, in step order) by point: each point's kernel
+time inside the sequence, beside its back-to-back time from the same line.
 """
 from __future__ import annotations
 
@@ -93,8 +101,56 @@ def table(trace_path, points_path, plain_path=None):
     return "\n".join(lines)
 
 
+def split_sequence(rows, names, dispatches, steps):
+    """{point name: per-call kernel ns} for the timed region of ``bench.py``:
+    the ``steps`` x len(names) calls after the last pair of consecutive
+    markers, the points in step order."""
+    pairs = [i for i in range(len(rows) - 1)
+             if MARKER in rows[i]["Kernel_Name"] and MARKER in rows[i + 1]["Kernel_Name"]]
+    if not pairs:
+        raise ValueError("no marker pair before the timed region")
+    i = pairs[-1] + 2
+    out = {n: [] for n in names}
+    for _ in range(steps):
+        for n in names:
+            seg = rows[i:i + dispatches[n]]
+            if len(seg) < dispatches[n] or any(MARKER in r["Kernel_Name"] for r in seg):
+                raise ValueError("timed region of the trace is incomplete")
+            out[n].append(sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in seg))
+            i += dispatches[n]
+    return out
+
+
+def sequence_table(trace_path, line_path):
+    """Per point of the bench step: kernel time inside the sequence (the
+    timed region of the traced run) beside the same kernel back to back
+    (``gated_points_kernel_us`` of the bench line, where present)."""
+    with open(line_path) as f:
+        line = json.loads([ln for ln in f.read().splitlines() if ln.strip().startswith("{")][-1])
+    names = [n.strip() for n in line["config"]["workload"].split(":", 1)[1].split(",")]
+    per = split_sequence(load_trace(trace_path), names, line["dispatches_per_call"],
+                         line["steps"])
+    alone = line.get("gated_points_kernel_us") or {}
+    lines = ["| point (in step order) | kernel µs in sequence (median) | mean | p90 | "
+             "back to back (events, median) | in sequence − back to back |",
+             "|---|---|---|---|---|---|"]
+    for n in names:
+        ns = sorted(per[n])
+        med = statistics.median(ns) / 1000.0
+        mean = statistics.mean(ns) / 1000.0
+        p90 = ns[min(len(ns) - 1, int(0.9 * len(ns)))] / 1000.0
+        a = alone.get(n, {}).get("kernel_us")
+        lines.append(f"| {n} | {med:.2f} | {mean:.2f} | {p90:.2f} | "
+                     f"{'-' if a is None else f'{a:.2f}'} | "
+                     f"{'-' if a is None else f'{med - a:+.2f}'} |")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     argv = sys.argv[1:] if argv is None else argv
+    if len(argv) == 3 and argv[0] == "--sequence":
+        print(sequence_table(argv[1], argv[2]))
+        return 0
     if len(argv) not in (2, 3):
         print(__doc__, file=sys.stderr)
         return 2

@@ -142,7 +142,7 @@ def test_even_backend_with_k_split():
     """SKG_BACKEND_EVEN with split_k = S: 256 x rb_per_wg workgroups are
     256 x rb_per_wg / S row blocks times S K slices (S must divide the
     workgroup count); each row block holds floor/ceil(N / blocks) rows; the
-    partials go through the workspace and a ticket per row block."""
+    slices' partials meet in the workspace's tree slots (S - 1 per output)."""
     mk = _capi.SkgConfig.make
     lib = _capi.lib()
 
@@ -154,8 +154,8 @@ def test_even_backend_with_k_split():
     c = mk(backend=skg.SKG_BACKEND_EVEN, inner=skg.SKG_INNER_MFMA_RING_GA, split_k=2,
            row_tiles=4, waves_n=1, waves_k=2, depth=2, rb_per_wg=1)
     assert geom(16, 14336, 7168, c)
-    # partials [128 blocks][2 slices][16 tokens][64 rows] fp32 + 128 tickets
-    assert skg.skinny_gemm_workspace_bytes(16, 14336, 7168, c) == 128 * 2 * 16 * 64 * 4 + 128 * 4
+    # tree slots [128 blocks][1 node][16 tokens][64 rows], 8 bytes each
+    assert skg.skinny_gemm_workspace_bytes(16, 14336, 7168, c) == 128 * 1 * 16 * 64 * 8
     # 32 rows cannot hold 56
     assert not geom(16, 14336, 7168, mk(backend=skg.SKG_BACKEND_EVEN,
                                         inner=skg.SKG_INNER_MFMA_RING_GA, split_k=2, row_tiles=2,
@@ -216,7 +216,11 @@ def test_workspace_bytes():
     sk = skg.SkgConfig.make(split_k=4, row_tiles=1, waves_k=4)
     rows = 4
     nrb = 256 // rows
-    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, sk) == nrb * 4 * 4 * rows * 4 + nrb * 4
+    # one pass: split_k - 1 = 3 tree nodes of one 8-byte slot per output
+    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, sk) == nrb * 3 * 4 * rows * 8
+    sk3 = skg.SkgConfig.make(split_k=3, row_tiles=1, waves_k=4)
+    assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, sk3) == nrb * 2 * 4 * rows * 8
+    # two passes: every slice's fp32 partials
     p2 = skg.SkgConfig.make(backend=skg.SKG_BACKEND_SPLITK_2PASS, split_k=4, row_tiles=1,
                             waves_k=4)
     assert skg.skinny_gemm_workspace_bytes(4, 7168, 256, p2) == nrb * 4 * 4 * rows * 4
@@ -410,10 +414,14 @@ def test_mid_tier_rules():
     st = mk(inner=F, row_tiles=1, depth=2, waves_n=1, waves_k=1)
     assert skg.skinny_gemm_check_config(64, 1024, 2112, st)
     assert not skg.skinny_gemm_check_config(64, 7168, 2112, st)
-    # the split-K workspace holds M rows of partials per block
+    # the split-K workspace holds M rows per block: 3 tree slots (8 bytes) per
+    # output in one pass, 4 partials (4 bytes) per output in two passes
     sk = mk(inner=GA, split_k=4, row_tiles=1, depth=2, waves_n=1, waves_k=1)
     nrb = -(-2112 // 16)
-    assert skg.skinny_gemm_workspace_bytes(48, 7168, 2112, sk) == nrb * 4 * 48 * 16 * 4 + nrb * 4
+    assert skg.skinny_gemm_workspace_bytes(48, 7168, 2112, sk) == nrb * 3 * 48 * 16 * 8
+    p2 = mk(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=GA, split_k=4, row_tiles=1, depth=2,
+            waves_n=1, waves_k=1)
+    assert skg.skinny_gemm_workspace_bytes(48, 7168, 2112, p2) == nrb * 4 * 48 * 16 * 4
 
 
 def test_mid_tier_dispatch_and_crossover_defaults():
@@ -546,7 +554,7 @@ def test_noalloc_scratch_covers_the_skinny_tier_and_rejects_larger_workspaces():
     fits the static scratch; a shape whose split-K workspace does not (the
     two-pass split of M = 48 at K = 7168, N = 2112) is rejected with
     SKG_ERR_SCRATCH_TOO_SMALL before any GPU work (placeholder pointers)."""
-    cap = skg.SKG_SCRATCH_PARTIAL_BYTES + 4 * skg.SKG_SCRATCH_TICKETS
+    cap = skg.SKG_SCRATCH_PARTIAL_BYTES + skg.SKG_SCRATCH_SLOT_BYTES
     for (K, N) in ((7168, 256), (7168, 384), (2880, 128), (7168, 2112), (1536, 24576),
                    (14336, 7168)):
         for M in range(1, 17):

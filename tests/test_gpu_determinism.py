@@ -87,8 +87,9 @@ def _repeat_identical(call, M, N, reps, what, batch=50):
 @pytest.mark.parametrize("M", [8, 16])
 @pytest.mark.parametrize("N", [256, 384])
 def test_router_split_k_thousands_of_calls(M, N):
-    """The router points that dispatch a single-pass K split (the ticket
-    and last-arriver sum): 2000 calls, every one bit-identical to the first."""
+    """The router points that dispatch a single-pass K split (the partials
+    combined along the exchange tree): 2000 calls, every one bit-identical to
+    the first."""
     A, B = _problem(M, 7168, N)
     cfg = skg.skinny_gemm_dispatch(M, 7168, N)
     assert cfg.split_k > 1 and cfg.backend != skg.SKG_BACKEND_SPLITK_2PASS, cfg

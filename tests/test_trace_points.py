@@ -64,3 +64,45 @@ def test_incomplete_trace_rejected(tmp_path):
     tr, pj = _write(tmp_path, rows[1:], {"a": _pt(0, 1)})
     with pytest.raises(ValueError):
         trace_points.split_points(trace_points.load_trace(tr), json.load(open(pj)))
+
+
+def test_sequence_split_takes_the_timed_region_after_the_marker_pair(tmp_path):
+    """The bench's timed region follows the last pair of marker calls; its
+    calls are attributed to the points in step order (a two-dispatch call
+    counts both), and dispatches before the pair are ignored."""
+    rows, t = [], 0
+
+    def add(name, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": f"skg::{name}", "Start_Timestamp": t,
+                     "End_Timestamp": t + dur})
+        t += dur + 10
+
+    add("a", 999)  # warm-up noise
+    add(trace_points.MARKER, 5)  # a lone marker is not the pair
+    add("b", 999)
+    add(trace_points.MARKER, 5)
+    add(trace_points.MARKER, 5)
+    for step in range(3):
+        add("p0", 1000 + step)
+        add("p1", 2000)
+        add("p1b", 500)  # second dispatch of p1
+    add("after", 999)  # later work (not in the timed region)
+    tr = tmp_path / "t_kernel_trace.csv"
+    with open(tr, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+    per = trace_points.split_sequence(trace_points.load_trace(str(tr)), ["P0", "P1"],
+                                      {"P0": 1, "P1": 2}, 3)
+    assert per == {"P0": [1000, 1001, 1002], "P1": [2500, 2500, 2500]}
+    line = tmp_path / "line.json"
+    line.write_text(json.dumps({"config": {"workload": "w: P0, P1"}, "steps": 3,
+                                "dispatches_per_call": {"P0": 1, "P1": 2},
+                                "gated_points_kernel_us": {"P1": {"kernel_us": 2.0}}}))
+    out = trace_points.sequence_table(str(tr), str(line))
+    assert "| P0 | 1.00 |" in out and "| P1 | 2.50 |" in out and "+0.50" in out
+    with pytest.raises(ValueError):
+        trace_points.split_sequence(trace_points.load_trace(str(tr)), ["P0", "P1"],
+                                    {"P0": 1, "P1": 2}, 4)

@@ -51,7 +51,7 @@ def test_noalloc_matches_allocating_entry_and_oracle(pair):
         cfg = skg.skinny_gemm_dispatch(M, K, N)
         print(f"noalloc M={M} K={K} N={N} cfg={cfg.as_tuple()}", flush=True)
         assert (skg.skinny_gemm_workspace_bytes(M, K, N, cfg)
-                <= skg.SKG_SCRATCH_PARTIAL_BYTES + 4 * skg.SKG_SCRATCH_TICKETS)
+                <= skg.SKG_SCRATCH_PARTIAL_BYTES + skg.SKG_SCRATCH_SLOT_BYTES)
         A_bits = inputs.make_a(M, K, N)
         B_bits = gu.cached_b(K, N)
         A, B = gu.operands(A_bits, B_bits, K)
@@ -72,8 +72,8 @@ def test_noalloc_matches_allocating_entry_and_oracle(pair):
 
 def test_noalloc_repeated_calls_identical():
     """Back-to-back split-K calls on one stream share the scratch: each one
-    leaves its arrival counters at zero for the next, so 500 calls in a row
-    give the first call's bits."""
+    leaves its tree slots empty for the next, so 500 calls in a row give the
+    first call's bits."""
     torch = gu.torch_cuda()
     M, K, N = 16, 7168, 256
     assert skg.skinny_gemm_dispatch(M, K, N).split_k > 1
