@@ -455,6 +455,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// The same with a run-time count: waits until at most r * L are outstanding
+// (0 <= r < R; r is wave-uniform).
+template <int L, int R>
+__device__ __forceinline__ void wait_vmcnt_steps(int r) {
+    if constexpr (R > 0) {
+        if (r == R - 1)
+            wait_vmcnt<(R - 1) * L>();
+        else
+            wait_vmcnt_steps<L, R - 1>(r);
+    }
+}
+
 template <int NV>
 __device__ __forceinline__ void staged_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -624,7 +636,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
     // Whole rounds of the ring: every slot is refilled unconditionally right
     // after it is consumed, so the compiler keeps each slot in the same
     // registers and waits for exactly that slot's loads.  The last round only
-    // consumes; refills for steps past T read A (see set_rows).
+    // consumes; refills for steps past T read A (see set_rows).  Refilling
+    // only while steps remain (no load left in flight at the end, as the LDS
+    // ring does) measured slower in this register ring, e.g. 8.34 -> 10.63 us
+    // on a 2 x 7168 x 2112 product; our reading is that the compiler's waits
+    // where the conditional refills join cover more loads than the slot's.
     const int TT = (T + PF - 1) / PF * PF;
     int t0 = 0;
     for (; t0 + PF < TT; t0 += PF) {
@@ -1005,10 +1021,14 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     const int rlw = wn * (16 * G);
 
     int cb = 0, cst = 0;
-    auto step = [&](int slot) {
-        // this slot's loads are the oldest; the other PF - 1 steps stay in flight
+    auto step = [&](int slot, int left) {
+        // this slot's loads are the oldest; the later steps (PF - 1 of them,
+        // or the `left` steps still to come near the end) stay in flight
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        wait_vmcnt<(PF - 1) * L>();
+        if (left >= PF - 1)
+            wait_vmcnt<(PF - 1) * L>();
+        else
+            wait_vmcnt_steps<L, PF - 1>(left);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const uint4 *tl = ring + slot * (NT * 256);
         // all operands first, so the reads go out back to back
@@ -1078,14 +1098,24 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
         }
     };
 
-    // whole rounds: every slot is refilled right after it is read (refills
-    // past T read A and are never consumed)
+    // whole rounds: every slot is refilled right after it is read, as long as
+    // steps remain (no load is issued that the wave does not consume, so the
+    // last step's wait is the wave's last).  The rounds in which every step
+    // refills run without the end-of-stream checks.
     const int TT = (T + PF - 1) / PF * PF;
-    for (int t0 = 0; t0 < TT; t0 += PF) {
+    int t0 = 0;
+    for (; t0 + 2 * PF <= T; t0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (t0 + i < T) step(i);
+            step(i, PF - 1);
             issue(i);
+        }
+    }
+    for (; t0 < TT; t0 += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            if (t0 + i < T) step(i, T - 1 - (t0 + i));
+            if (t0 + i + PF < T) issue(i);
         }
     }
     // no LDS write may still be on its way when the workgroup's LDS is reused
