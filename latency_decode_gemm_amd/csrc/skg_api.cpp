@@ -283,6 +283,9 @@ int run(const void *A, const void *B, void *C, int M, int N, int K, int64_t lda,
     p.waves_k = cfg.waves_k;
     p.rows_per_wg = g.rows_per_wg;
     p.num_rb = g.num_rb;
+    p.even_q = g.num_rb > 0 ? N / g.num_rb : 0;
+    p.even_r = g.num_rb > 0 ? N % g.num_rb : 0;
+    p.grid_rb = g.grid_rb;
     p.lds_stride = g.lds_stride;
     p.stash_offset = g.stash_offset;
     p.tr_offset = g.tr_offset;

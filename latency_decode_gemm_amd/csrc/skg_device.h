@@ -222,7 +222,7 @@ __device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *rowp, int c, co
 // in the tail form above.  The caller's barrier waits for all of it.
 __device__ __forceinline__ void stage_a(const KParams &p, uint16_t *As, int wg_c0) {
     const int lane = threadIdx.x & 63;
-    const int nwaves = blockDim.x >> 6;
+    const int nwaves = p.waves_n * p.waves_k;
     const int nch = p.wg_chunks;
     const int nblk = (nch + 63) >> 6;  // 64-chunk blocks per row
     for (int blk = threadIdx.x >> 6; blk < p.M * nblk; blk += nwaves) {
@@ -329,8 +329,11 @@ __device__ __forceinline__ unsigned long long slot_word(float v, int side) {
 // count - 1; stores take local rows < count only.
 __device__ __forceinline__ void block_rows(const KParams &p, int rb, int &start, int &count) {
     if (p.even) {
-        start = (int)(((int64_t)rb * p.N) / p.num_rb);
-        count = (int)(((int64_t)(rb + 1) * p.N) / p.num_rb) - start;
+        // rb N / num_rb = rb q + rb r / num_rb with N = q num_rb + r; rb r <
+        // num_rb^2 <= 2^28, so 32-bit unsigned arithmetic is exact
+        const unsigned nrb = (unsigned)p.num_rb, r = (unsigned)p.even_r;
+        start = rb * p.even_q + (int)(((unsigned)rb * r) / nrb);
+        count = p.even_q + (int)(((unsigned)(rb + 1) * r) / nrb - ((unsigned)rb * r) / nrb);
     } else {
         start = rb * p.rows_per_wg;
         count = min(p.rows_per_wg, p.N - start);
@@ -388,7 +391,7 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
     const int S = p.split_k;
     w.rb0 = blockIdx.x / S;
     w.s = blockIdx.x - w.rb0 * S;
-    w.rbs = gridDim.x / S;
+    w.rbs = p.grid_rb;
     w.nblk = w.rb0 < p.num_rb ? (p.num_rb - w.rb0 + w.rbs - 1) / w.rbs : 0;
     w.wg_c0 = w.s * p.wg_chunks;
     return w;
@@ -418,7 +421,7 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
     // thread -> local row rl and tokens m0, m0 + mstep, ...
     const int m0 = threadIdx.x / NB;
     const int rl = threadIdx.x - m0 * NB;
-    const int mstep = blockDim.x / NB;
+    const int mstep = 64 * p.waves_n * p.waves_k / NB;
     for (int b = 0; b < w.nblk; ++b) {
         const int rb = w.rb0 + b * w.rbs;
         int bst, bcnt;
@@ -674,7 +677,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 template <bool RAW = false, int MT = 1>
 __device__ __forceinline__ void stage_a_frag(const KParams &p, uint16_t *As, int wg_c0) {
     const int lane = threadIdx.x & 63;
-    const int nwaves = blockDim.x >> 6;
+    const int nwaves = p.waves_n * p.waves_k;
     const int nblk = (p.wg_chunks >> 2) * MT;  // (32-wide step, token tile) blocks
     for (int blk = threadIdx.x >> 6; blk < nblk; blk += nwaves) {
         const int mt = blk % MT;

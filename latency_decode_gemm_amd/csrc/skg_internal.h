@@ -41,11 +41,13 @@ struct KParams {
     int split_k;      // workgroups along K per row block
     int two_pass;     // split-K partials are summed by a second kernel
     int even;         // SKG_BACKEND_EVEN: row block rb is rows [rb N / num_rb, (rb + 1) N / num_rb)
+    int even_q, even_r; // N = even_q num_rb + even_r (SKG_BACKEND_EVEN)
     int wg_chunks;    // chunks per split (multiple of wave_chunks)
     int wave_chunks;  // chunks per K-wave (multiple of the K-step)
-    int waves_n, waves_k;
+    int waves_n, waves_k; // the workgroup's waves (64 * waves_n * waves_k threads)
     int rows_per_wg;
     int num_rb;
+    int grid_rb;      // workgroups per K slice (the grid is grid_rb x split_k)
     int lds_stride;   // bf16 elements per staged A row in LDS
     int stash_offset; // byte offset in LDS of the per-row-block partial sums
                       // that the epilogue combines
