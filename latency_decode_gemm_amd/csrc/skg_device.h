@@ -402,16 +402,30 @@ __device__ __forceinline__ WgPlan wg_plan(const KParams &p) {
 // that wave's registers.  Otherwise (waves_k > 1, or the single-pass split-K
 // backend, which combines per output) each wave parks its partial sums of
 // each row block in LDS (the stash), and after the stream the workgroup's
-// threads take (token, local row) pairs, consecutive threads consecutive
-// rows, add the waves_k partials in wave order, and write C (split_k == 1),
-// the split's partial (two-pass), or combine it with the other slices'
-// (splitk_combine; the thread that completes the sum writes C).
-// base(b, q, rl) is the stash index of token 0 of (row block b, K-wave q,
-// local row rl); mofs(m) adds token m.
+// threads add the waves_k partials of an output in wave order and write C
+// (split_k == 1), the split's partial (two-pass), or combine it with the other
+// slices' (splitk_combine; the thread that completes the sum writes C).
 __device__ __forceinline__ bool direct_write(const KParams &p) {
     return p.waves_k == 1 && (p.split_k == 1 || p.two_pass);
 }
 
+// The workgroup's K-wave sum v of output (token m, local row rl) of row block
+// rb (rows [bst, bst + bcnt)).
+__device__ __forceinline__ void finish_output(const KParams &p, const WgPlan &w, int rb, int bst,
+                                              int bcnt, int m, int rl, float v) {
+    if (p.split_k == 1) {
+        if (rl < bcnt) store_c(p, m, bst + rl, v);
+    } else if (p.two_pass) {
+        p.ws[((size_t)(rb * p.split_k + w.s) * p.M + m) * p.rows_per_wg + rl] = v;
+    } else if (rl < bcnt) {
+        if (splitk_combine(p, rb, w.s, m, rl, v)) store_c(p, m, bst + rl, v);
+    }
+}
+
+// VALU kernels: the stash is [row block][K-wave][m][local row]; threads take
+// (token, local row) pairs, consecutive threads consecutive rows.  base(b, q,
+// rl) is the stash index of token 0 of (row block b, K-wave q, local row rl);
+// mofs(m) adds token m.
 template <class BASE, class MOFS>
 __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, const float *stash,
                                              BASE base, MOFS mofs) {
@@ -429,12 +443,69 @@ __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, 
         for (int m = m0; m < M; m += mstep) {
             float v = stash[base(b, 0, rl) + mofs(m)];
             for (int q = 1; q < p.waves_k; ++q) v += stash[base(b, q, rl) + mofs(m)];
-            if (p.split_k == 1) {
-                if (rl < bcnt) store_c(p, m, bst + rl, v);
-            } else if (p.two_pass) {
-                p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] = v;
-            } else if (rl < bcnt) {
-                if (splitk_combine(p, rb, w.s, m, rl, v)) store_c(p, m, bst + rl, v);
+            finish_output(p, w, rb, bst, bcnt, m, rl, v);
+        }
+    }
+}
+
+// Matrix-core kernels: each wave parks its accumulators in their fragment
+// layout, f32x4 number (((b waves_k + q) waves_n + wq) G + t) MT + mt) 64 +
+// lane for row block b, K-wave q, N-wave wq, row tile t and token tile mt;
+// lane 16 hi + lo holds tokens 16 mt + 4 hi + j (j = 0..3) of local row
+// 16 G wq + 16 t + lo.  With no more threads than fragments, threads take
+// whole fragments: every stash read is one 16-byte read by consecutive lanes
+// (no bank conflicts), the waves_k partials added element by element in wave
+// order.  With more threads than fragments (several K-waves per row tile),
+// each thread takes single outputs, consecutive threads consecutive rows, so
+// that the outputs' chains of exchanges under the single-pass split run side
+// by side; those reads hit a bank several times, but there are few per thread.
+template <int G, int MT>
+__device__ __forceinline__ void write_blocks_frag(const KParams &p, const WgPlan &w,
+                                                  const f32x4_t *stash) {
+    __syncthreads();
+    const int nthr = 64 * p.waves_n * p.waves_k;
+    const int per_q = p.waves_n * G * MT * 64;  // fragments of one K-wave and row block
+    if (nthr > per_q) {
+        const float *sf = reinterpret_cast<const float *>(stash);
+        const int NB = p.rows_per_wg;  // 16 G waves_n <= the workgroup's threads
+        const int m0 = threadIdx.x / NB;
+        const int rl = threadIdx.x - m0 * NB;
+        const int mstep = nthr / NB;
+        const int wq = rl / (16 * G);
+        const int t = (rl >> 4) % G;
+        for (int b = 0; b < w.nblk; ++b) {
+            const int rb = w.rb0 + b * w.rbs;
+            int bst, bcnt;
+            block_rows(p, rb, bst, bcnt);
+            for (int m = m0; m < p.M; m += mstep) {
+                // fragment (b, q, wq, t, m / 16), lane 16 ((m & 15) / 4) + (rl & 15), element m & 3
+                const int f0 = ((b * p.waves_k * p.waves_n + wq) * G + t) * MT + (m >> 4);
+                const int el = (16 * ((m & 15) >> 2) + (rl & 15)) * 4 + (m & 3);
+                float v = sf[f0 * 256 + el];
+                for (int q = 1; q < p.waves_k; ++q) v += sf[(f0 + q * p.waves_n * G * MT) * 256 + el];
+                finish_output(p, w, rb, bst, bcnt, m, rl, v);
+            }
+        }
+        return;
+    }
+    for (int b = 0; b < w.nblk; ++b) {
+        const int rb = w.rb0 + b * w.rbs;
+        int bst, bcnt;
+        block_rows(p, rb, bst, bcnt);
+        for (int e = threadIdx.x; e < per_q; e += nthr) {
+            const f32x4_t *src = stash + (size_t)b * p.waves_k * per_q + e;
+            f32x4_t v = src[0];
+            for (int q = 1; q < p.waves_k; ++q) v += src[q * per_q];
+            const int lane = e & 63;
+            const int r = e >> 6;
+            const int mt = r % MT;
+            const int tt = (r / MT) % G;
+            const int wn = r / (MT * G);
+            const int rlf = 16 * G * wn + 16 * tt + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = 16 * mt + 4 * (lane >> 4) + j;
+                if (m < p.M) finish_output(p, w, rb, bst, bcnt, m, rlf, v[j]);
             }
         }
     }
@@ -911,15 +982,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
             issue(buf[i], abuf[i]);
         }
     }
-    if (!direct)
-        write_blocks(
-            p, w, stash,
-            [&](int b, int q, int rl) {
-                const int wq = rl / (16 * G);  // N-wave
-                const int t = (rl >> 4) % G;   // tile
-                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * MT * 256 + (rl & 15) * 4;
-            },
-            [&](int m) { return 256 * (m >> 4) + 64 * ((m & 15) >> 2) + (m & 3); });
+    if (!direct) write_blocks_frag<G, MT>(p, w, reinterpret_cast<const f32x4_t *>(stash));
 }
 
 // ---- MFMA kernel with an LDS ring --------------------------------------------
@@ -1123,15 +1186,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     }
     // no LDS write may still be on its way when the workgroup's LDS is reused
     wait_vmcnt<0>();
-    if (!direct)
-        write_blocks(
-            p, w, stash,
-            [&](int b, int q, int rl) {
-                const int wq = rl / (16 * G);  // N-wave
-                const int t = (rl >> 4) % G;   // tile
-                return (((b * p.waves_k + q) * p.waves_n + wq) * G + t) * MT * 256 + (rl & 15) * 4;
-            },
-            [&](int m) { return 256 * (m >> 4) + 64 * ((m & 15) >> 2) + (m & 3); });
+    if (!direct) write_blocks_frag<G, MT>(p, w, reinterpret_cast<const f32x4_t *>(stash));
 }
 
 // Over fp32 weights the register ring is twice as large, and these
