@@ -551,17 +551,27 @@ def test_noalloc_checks_arguments_like_the_allocating_entry():
 
 def test_noalloc_scratch_covers_the_skinny_tier_and_rejects_larger_workspaces():
     """Every configuration dispatch returns for M <= 16 on the workload shapes
-    fits the static scratch; a shape whose split-K workspace does not (the
-    two-pass split of M = 48 at K = 7168, N = 2112) is rejected with
-    SKG_ERR_SCRATCH_TOO_SMALL before any GPU work (placeholder pointers)."""
-    cap = skg.SKG_SCRATCH_PARTIAL_BYTES + skg.SKG_SCRATCH_SLOT_BYTES
+    fits the static scratch (tree slots of a one-pass split within
+    SKG_SCRATCH_SLOT_BYTES, partials of a two-pass split within
+    SKG_SCRATCH_PARTIAL_BYTES), so the no-allocation entry point does not
+    refuse it; a shape whose split-K workspace does not fit (the two-pass split
+    of M = 64 at K = 7168, N = 2112) is rejected with SKG_ERR_SCRATCH_TOO_SMALL
+    before any GPU work (placeholder pointers)."""
+    largest = 0
     for (K, N) in ((7168, 256), (7168, 384), (2880, 128), (7168, 2112), (1536, 24576),
                    (14336, 7168)):
         for M in range(1, 17):
             cfg = skg.skinny_gemm_dispatch(M, K, N)
-            assert skg.skinny_gemm_workspace_bytes(M, K, N, cfg) <= cap // 8, (M, K, N)
-    M, K, N = 48, 7168, 2112
+            need = skg.skinny_gemm_workspace_bytes(M, K, N, cfg)
+            limit = (skg.SKG_SCRATCH_PARTIAL_BYTES if cfg.backend == skg.SKG_BACKEND_SPLITK_2PASS
+                     else skg.SKG_SCRATCH_SLOT_BYTES)
+            assert need <= limit, (M, K, N, cfg, need)
+            assert _noalloc(M=M, K=K, N=N, lda=K, ldb=K, ldc=N) != skg.SKG_ERR_SCRATCH_TOO_SMALL
+            largest = max(largest, need)
+    assert largest > 0  # some dispatched configuration does split K
+    M, K, N = 64, 7168, 2112
     cfg = skg.skinny_gemm_dispatch(M, K, N)
+    assert cfg.backend == skg.SKG_BACKEND_SPLITK_2PASS, cfg
     assert skg.skinny_gemm_workspace_bytes(M, K, N, cfg) > skg.SKG_SCRATCH_PARTIAL_BYTES
     assert _noalloc(M=M, K=K, N=N, lda=K, ldb=K, ldc=N) == skg.SKG_ERR_SCRATCH_TOO_SMALL
     assert "static scratch" in skg.skinny_gemm_strerror(skg.SKG_ERR_SCRATCH_TOO_SMALL)

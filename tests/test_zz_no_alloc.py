@@ -35,9 +35,10 @@ PAIRS = [
     ((8, 7168, 384, "f32", None), (5, 7168, 256, "f32", None)),
     # split 4 (M = 16) then split 2 (M = 8): another geometry in the same scratch
     ((16, 7168, 256, "f32", None), (8, 7168, 256, "f32", None)),
-    # middle-tier splits (two token tiles: 4 splits, one K-wave per slice)
+    # middle-tier splits (two token tiles, 4 splits)
     ((32, 7168, 384, "f32", None), (24, 7168, 256, "f32", None)),
-    # no K split: the scratch is not touched; bf16 into a strided buffer
+    # qkv_a-style, bf16 into a strided buffer: a 3-way split, then none (the
+    # scratch is not touched)
     ((16, 7168, 2112, "bf16", 4096), (3, 7168, 2112, "bf16", 4096)),
 ]
 
@@ -95,11 +96,12 @@ def test_noalloc_repeated_calls_identical():
 
 
 def test_noalloc_rejects_a_workspace_beyond_the_scratch():
-    """The two-pass split of qkv_a-style M = 48 needs more partials than the
+    """The two-pass split of qkv_a-style M = 64 needs more partials than the
     scratch holds: SKG_ERR_SCRATCH_TOO_SMALL, and the output is untouched."""
     torch = gu.torch_cuda()
-    M, K, N = 48, 7168, 2112
+    M, K, N = 64, 7168, 2112
     cfg = skg.skinny_gemm_dispatch(M, K, N)
+    assert cfg.backend == skg.SKG_BACKEND_SPLITK_2PASS, cfg
     assert skg.skinny_gemm_workspace_bytes(M, K, N, cfg) > skg.SKG_SCRATCH_PARTIAL_BYTES
     A = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     B = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
