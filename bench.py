@@ -94,6 +94,10 @@ def parse():
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the per-point report of the points the bandwidth target "
                          "covers (N*K >= 7168*2112), timed after the headline region")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="host only: from the counter collections of two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, then WRITE_SIZE) of `--only M,K,N --copy-probe-mb MB`, "
+                         "write that point's HBM bytes per launch to profiles/traffic.json")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -459,8 +463,87 @@ def load_traffic(dominant_name, config):
     return entry.get("hbm_bytes_per_launch")
 
 
+def counter_per_dispatch(path, counter):
+    """{dispatch id: [kernel name, counter summed over its instances]} from a
+    rocprofv3 counter-collection CSV."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], [r["Kernel_Name"], 0.0])
+            d[1] += float(r["Counter_Value"])
+    return per
+
+
+def write_traffic(args):
+    """HBM bytes per launch of the --only point's kernel: the median FETCH_SIZE
+    and WRITE_SIZE (KiB) over its dispatches, each scaled by known bytes over
+    what the same counter reads for the copy probe of the same run (the largest
+    runtime copy: args.copy_probe_mb MiB read and written)."""
+    from statistics import median
+
+    import latency_decode_gemm_amd as skg
+    from latency_decode_gemm_amd import inputs
+    if not args.only or not args.copy_probe_mb:
+        sys.exit("bench.py: --write-traffic needs --only M,K,N and --copy-probe-mb")
+    M, K, N = (int(x) for x in args.only.split(","))
+    p = [q for q in inputs.all_points() if (q["M"], q["K"], q["N"]) == (M, K, N)][0]
+    cfg = skg.skinny_gemm_dispatch(M, K, N)
+    probe = args.copy_probe_mb << 20
+    out = {}
+    for path, counter in zip(args.write_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
+        per = counter_per_dispatch(path, counter)
+        copies = [v for k, v in per.values() if "copyBuffer" in k]
+        # the GEMM kernels are the templates (skg_valu_kernel<...>, skg_mfma_...<...>);
+        # the zero-fill marker and the scratch clear are not
+        gemm = [(k, v) for k, v in per.values() if "skg_" in k and "_kernel<" in k]
+        names = {k for k, _ in gemm}
+        if not copies or len(names) != 1:
+            sys.exit(f"bench.py: {path}: expected one GEMM kernel and the copy probe, "
+                     f"found {sorted(names)} and {len(copies)} copies")
+        kib = median(v for _, v in gemm)
+        scale = probe / (max(copies) * 1024)
+        out[counter] = (names.pop(), kib, scale, len(gemm))
+    kernel = out["FETCH_SIZE"][0]
+    s_out = 2 if p["out"] == "bf16" else 4
+    alg = 2 * N * K + 2 * M * K + M * N * s_out
+    fb = round(out["FETCH_SIZE"][1] * 1024 * out["FETCH_SIZE"][2])
+    wb = round(out["WRITE_SIZE"][1] * 1024 * out["WRITE_SIZE"][2])
+    name = f"M{M}_K{K}_N{N}_{p['out']}" + (f"_ldc{p['ldc']}" if p["ldc"] and p["ldc"] != N else "")
+    rec = {
+        "about": "HBM bytes per launch of the dominant bench kernel from rocprofv3 --pmc "
+                 "FETCH_SIZE and WRITE_SIZE (separate runs), each scaled by the same counter on "
+                 f"a {args.copy_probe_mb} MiB device copy in the same run; written by "
+                 "bench.py --write-traffic",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_scale": round(out["FETCH_SIZE"][2], 5),
+        "write_scale": round(out["WRITE_SIZE"][2], 5),
+        "points": {name: {
+            "kernel": kernel.replace("void skg::(anonymous namespace)::", "").split("(")[0],
+            "config": cfg.as_dict(),
+            "dispatches": out["FETCH_SIZE"][3],
+            "fetch_kib_raw": out["FETCH_SIZE"][1],
+            "write_kib_raw": out["WRITE_SIZE"][1],
+            "fetch_bytes": fb,
+            "write_bytes": wb,
+            "hbm_bytes_per_launch": fb + wb,
+            "algorithmic_bytes": alg,
+            "traffic_over_algorithmic": round((fb + wb) / alg, 3),
+        }},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["points"][name]))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: the GEMM runs on one GPU (asked for --gpus {args.gpus}); sharding "
               "it across GPUs (by rows of the weights, or by K with one all-reduce) is not "
