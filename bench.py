@@ -64,7 +64,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_lo.hip",
                   "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_f32w_lo.hip", "skg_f32w_hi.hip",
                   "skg_f32w_ga.hip", "skg_mfma_mid.h", "skg_mfma_mt2.hip", "skg_mfma_mt3.hip",
-                  "skg_mfma_mt4.hip", "skg_api.cpp"]
+                  "skg_mfma_mt4.hip", "skg_mfma_sync.hip", "skg_api.cpp"]
 F32W_SUFFIX = "_w32"  # point names of the fp32-weight router GEMM
 
 

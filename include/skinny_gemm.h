@@ -126,9 +126,17 @@ typedef enum {
     SKG_INNER_MFMA_RING = 4,    /* as SKG_INNER_MFMA, with the weight loads
                                    written straight into LDS tiles (a ring of
                                    depth K steps per wave) instead of registers */
-    SKG_INNER_MFMA_RING_GA = 5  /* as SKG_INNER_MFMA_GA, with weights and
+    SKG_INNER_MFMA_RING_GA = 5, /* as SKG_INNER_MFMA_GA, with weights and
                                    activation fragments both loaded straight
                                    into the LDS ring */
+    SKG_INNER_MFMA_RING_SYNC = 6,   /* as SKG_INNER_MFMA_RING_GA, with the
+                                       workgroup's waves meeting at a barrier
+                                       every K step; M <= 16, row_tiles 1 or 2 */
+    SKG_INNER_MFMA_RING_SHARED = 7  /* as SKG_INNER_MFMA_RING_SYNC, with each K
+                                       step's activation tile loaded once per
+                                       workgroup (per group of waves on the
+                                       same K range) into an LDS ring its waves
+                                       share; depth >= 3 */
 } skg_inner;
 
 #define SKG_MAX_M 64      /* the matrix-core kinds; the VALU kinds take M <= 16 */

@@ -8,7 +8,8 @@ tensors into that ABI.  ``inputs`` holds the seeded synthetic-input recipe.
 from ._capi import (SKG_BACKEND_DOT, SKG_BACKEND_EVEN, SKG_BACKEND_SPLITK, SKG_BACKEND_SPLITK_2PASS, SKG_ERR_HIP, SKG_ERR_INVALID_ARG,
                     SKG_ERR_MISALIGNED, SKG_ERR_NO_DEVICE, SKG_ERR_NOT_WARMED, SKG_ERR_SCRATCH_TOO_SMALL,
                     SKG_ERR_UNSUPPORTED, SKG_INNER_MFMA, SKG_INNER_MFMA_GA,
-                    SKG_INNER_MFMA_RING, SKG_INNER_MFMA_RING_GA, SKG_INNER_VALU,
+                    SKG_INNER_MFMA_RING, SKG_INNER_MFMA_RING_GA, SKG_INNER_MFMA_RING_SHARED,
+                    SKG_INNER_MFMA_RING_SYNC, SKG_INNER_VALU,
                     SKG_INNER_VALU_GA, SKG_MAX_M, SKG_MAX_M_VALU, SKG_OK,
                     SKG_OUT_BF16, SKG_OUT_F32, SKG_SCRATCH_PARTIAL_BYTES, SKG_SCRATCH_SLOT_BYTES,
                     HipEvent, SkgConfig, SkinnyGemmError)

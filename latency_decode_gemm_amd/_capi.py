@@ -34,6 +34,8 @@ SKG_INNER_MFMA_GA = 2
 SKG_INNER_VALU_GA = 3
 SKG_INNER_MFMA_RING = 4
 SKG_INNER_MFMA_RING_GA = 5
+SKG_INNER_MFMA_RING_SYNC = 6
+SKG_INNER_MFMA_RING_SHARED = 7
 SKG_MAX_M = 64
 SKG_MAX_M_VALU = 16
 SKG_SCRATCH_SLOT_BYTES = 1 << 20
@@ -43,6 +45,10 @@ SKG_SCRATCH_PARTIAL_BYTES = 1 << 20
 VALU_VARIANTS = ((1, 4), (1, 8), (1, 12), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4))
 MFMA_VARIANTS = ((1, 2), (1, 3), (1, 4), (1, 6), (2, 1), (2, 2), (2, 3), (2, 4), (4, 1),
                  (4, 2))
+# the barrier kinds (M <= 16): SKG_INNER_MFMA_RING_SYNC, and the shared
+# activation ring SKG_INNER_MFMA_RING_SHARED (depth >= 3)
+SYNC_VARIANTS = ((1, 2), (1, 3), (1, 4), (1, 6), (2, 1), (2, 2), (2, 3), (2, 4))
+SHARED_VARIANTS = tuple(v for v in SYNC_VARIANTS if v[1] >= 3)
 
 # Every function the header declares, with (restype, argtypes).
 _i = ctypes.c_int

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libskinny_gemm.so")
 
 SOURCES = ["skg_valu_lo.hip", "skg_valu_hi.hip", "skg_valu_ga.hip", "skg_f32w_lo.hip",
            "skg_f32w_hi.hip", "skg_f32w_ga.hip", "skg_mfma_mt2.hip", "skg_mfma_mt3.hip",
-           "skg_mfma_mt4.hip", "skg_launch.hip", "skg_scratch.hip", "skg_api.cpp"]
+           "skg_mfma_mt4.hip", "skg_mfma_sync.hip", "skg_launch.hip", "skg_scratch.hip",
+           "skg_api.cpp"]
 HEADERS = ["skg_device.h", "skg_mfma_mid.h", "skg_internal.h", "tuned_table.inc", "tuned_table_f32w.inc",
            "crossover_table.inc",
            os.path.join("..", "..", "include", "skinny_gemm.h")]

@@ -322,10 +322,14 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     } else {
         return false;
     }
-    if (cfg.inner < SKG_INNER_VALU || cfg.inner > SKG_INNER_MFMA_RING_GA) return false;
-    const bool ring = cfg.inner == SKG_INNER_MFMA_RING || cfg.inner == SKG_INNER_MFMA_RING_GA;
+    if (cfg.inner < SKG_INNER_VALU || cfg.inner > SKG_INNER_MFMA_RING_SHARED) return false;
+    const bool ring = cfg.inner == SKG_INNER_MFMA_RING || cfg.inner == SKG_INNER_MFMA_RING_GA ||
+                      cfg.inner == SKG_INNER_MFMA_RING_SYNC ||
+                      cfg.inner == SKG_INNER_MFMA_RING_SHARED;
     const bool lds_frag = cfg.inner == SKG_INNER_MFMA || cfg.inner == SKG_INNER_MFMA_RING;
     const bool valu = cfg.inner == SKG_INNER_VALU || cfg.inner == SKG_INNER_VALU_GA;
+    // the activation tile of a step shared by the workgroup's waves
+    const bool shared_a = cfg.inner == SKG_INNER_MFMA_RING_SHARED;
     // VALU_GA keeps depth x M activation chunks in registers
     if (cfg.inner == SKG_INNER_VALU_GA && (M > 8 || M * cfg.depth > 32)) return false;
     if (valu && M > kMaxMValu) return false;
@@ -369,10 +373,13 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     if (a_bytes > (size_t)kMaxLdsBytes) return false;
     r.tr_offset = (int)((a_bytes + 15) / 16 * 16);
     // MFMA: one transpose tile per 16-row tile of B per wave, plus one per
-    // token tile for A (GA) (the LDS ring: depth slots of those tiles)
-    const int tiles = (valu ? 0 : lds_frag ? cfg.row_tiles : cfg.row_tiles + mt) *
+    // token tile for A (GA) (the LDS ring: depth slots of those tiles); with
+    // the shared activation ring, the waves' rings hold B only and depth x
+    // waves_k activation tiles follow them
+    const int tiles = (valu ? 0 : (lds_frag || shared_a) ? cfg.row_tiles : cfg.row_tiles + mt) *
                       (ring ? cfg.depth : 1);
-    const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes;
+    const size_t tr_bytes = (size_t)cfg.waves_n * cfg.waves_k * tiles * kTileBytes +
+                            (shared_a ? (size_t)cfg.depth * cfg.waves_k * mt * kTileBytes : 0);
     r.stash_offset = (int)(r.tr_offset + tr_bytes);
     // stash: every wave's partial sums of each of the workgroup's row blocks
     // (VALU: M x its rows; MFMA: one 16 x 16 fp32 tile per 16 rows and

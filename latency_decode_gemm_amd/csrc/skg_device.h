@@ -998,12 +998,27 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 // operands as they are read.  Tokens m >= M read row M - 1 of A and produce
 // accumulator rows that are never stored (an MFMA output row depends on its
 // own activation row only).
-template <int G, int PF, int AQ, int MT = 1>
+// SY (with activations loaded per step, AQ > 0): 0, the waves run freely; 1,
+// the workgroup's waves meet at a barrier every K step (their loads of
+// neighbouring rows at the same K then reach memory together, measured
+// faster on some shapes); 2, as 1, and each step's activation tile is loaded
+// once per workgroup (by the waves with wn == 0, one per K-wave group) into a
+// ring the waves share, instead of once per wave.  A shared slot can only be
+// refilled when every wave has read it, i.e. after the next step's barrier,
+// so with SY = 2 a step first waits for its own loads, meets the others, then
+// refills the slot the previous step used (depth >= 3 keeps depth - 2 steps
+// in flight behind the one being read).  Every wave of a workgroup runs the
+// same number of steps, so all of them reach every barrier.
+template <int G, int PF, int AQ, int MT = 1, int SY = 0>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p) {
     constexpr bool AG = AQ > 0;
+    constexpr bool SH = SY == 2;
     static_assert(MT == 1 || AQ == 0 || AQ == 4, "several token tiles load whole tiles");
-    constexpr int NT = G + (AG ? MT : 0);  // tiles per ring slot
-    constexpr int L = 4 * G + MT * AQ;     // loads per K step
+    static_assert(SY == 0 || (AG && MT == 1), "barrier modes take per-step activations, M <= 16");
+    static_assert(!SH || PF >= 3, "a shared ring needs depth >= 3");
+    constexpr int NT = G + ((AG && !SH) ? MT : 0);  // tiles per ring slot of a wave
+    constexpr int LB = 4 * G;                        // weight loads per K step
+    constexpr int L = LB + MT * AQ;                  // loads per K step with the activations
     static_assert((PF - 1) * L < 64 && PF * L < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *As = reinterpret_cast<uint16_t *>(smem);
@@ -1023,6 +1038,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     const int wv_c0 = w.wg_c0 + wk * p.wave_chunks;
     const int tail_st = max(0, (p.nfull - wv_c0) / kValuStep);
     uint4 *ring = reinterpret_cast<uint4 *>(smem + p.tr_offset) + wave * (PF * NT * 256);
+    // SY = 2: the shared activation ring after all waves' rings, slot s of
+    // K-wave group wk at tile (s * waves_k + wk); loaded by the wn == 0 waves
+    const uint4 *aring = reinterpret_cast<const uint4 *>(smem + p.tr_offset) +
+                         p.waves_n * p.waves_k * (PF * NT * 256);
+    const bool loader = !SH || wn == 0;
     // chunk of the step fetched by this lane for DMA block q
     int swz[4];
 #pragma unroll
@@ -1047,8 +1067,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
                                  : p.A;
     };
     const uint32_t ring_addr = lds_addr_of(ring);
+    const uint32_t aring_addr = lds_addr_of(aring);
     auto issue = [&](int slot) {
         const uint32_t dst = ring_addr + slot * (NT * kTileBytes);
+        const uint32_t adst =
+            SH ? aring_addr + (slot * p.waves_k + wk) * kTileBytes : dst + G * kTileBytes;
         const int cb0 = wv_c0 + lst * kValuStep;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1056,12 +1079,14 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
 #pragma unroll
             for (int t = 0; t < G; ++t)
                 lds_dma16_raw<true>(rowp[t][q] + off, dst + t * kTileBytes + 1024 * q);
-            if constexpr (AG)
+            if constexpr (AG) {
+                if (loader)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    if (q < AQ)
-                        lds_dma16_raw<false>(arow[mt * AQ + q] + off,
-                                             dst + (G + mt) * kTileBytes + 1024 * q);
+                    for (int mt = 0; mt < MT; ++mt)
+                        if (q < AQ)
+                            lds_dma16_raw<false>(arow[mt * AQ + q] + off,
+                                                 adst + mt * kTileBytes + 1024 * q);
+            }
         }
         if (++lst == SPB) {
             lst = 0;
@@ -1087,23 +1112,22 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     const int rlw = wn * (16 * G);
 
     int cb = 0, cst = 0;
-    auto step = [&](int slot, int left) {
-        // this slot's loads are the oldest; the later steps (PF - 1 of them,
-        // or the `left` steps still to come near the end) stay in flight
+    // the workgroup's waves meet (their earlier LDS reads complete first)
+    auto meet = [&]() {
+        __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+        __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (left >= PF - 1)
-            wait_vmcnt<(PF - 1) * L>();
-        else
-            wait_vmcnt_steps<L, PF - 1>(left);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto compute = [&](int slot) {
         const uint4 *tl = ring + slot * (NT * 256);
+        const uint4 *atl = SH ? aring + (slot * p.waves_k + wk) * (MT * 256) : tl + G * 256;
         // all operands first, so the reads go out back to back
         uint4 av[4][MT], bv[4][G];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                av[s][mt] = AG ? tl[(G + mt) * 256 + tile_slot(lo, 4 * s + hi)]
+                av[s][mt] = AG ? atl[mt * 256 + tile_slot(lo, 4 * s + hi)]
                                : lds16(ap + ((cst * 4 + s) * MT + mt) * (64 * kChunk));
 #pragma unroll
             for (int t = 0; t < G; ++t) bv[s][t] = tl[t * 256 + tile_slot(lo, 4 * s + hi)];
@@ -1163,7 +1187,36 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
             ++cb;
         }
     };
+    auto step = [&](int slot, int left) {
+        // this slot's loads are the oldest; the later steps (PF - 1 of them,
+        // or the `left` steps still to come near the end) stay in flight
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (left >= PF - 1)
+            wait_vmcnt<(PF - 1) * L>();
+        else
+            wait_vmcnt_steps<L, PF - 1>(left);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (SY == 1) meet();
+        compute(slot);
+    };
 
+    if constexpr (SH) {
+        // refills after the barrier: step t - 1 + PF into the slot step t - 1
+        // used, so behind step t's loads there are PF - 2 steps in flight (PF
+        // - 1 at the first step), each of L loads for a loading wave, LB for
+        // the others
+        for (int t = 0; t < T; ++t) {
+            const int after = t == 0 ? min(PF - 1, T - 1) : min(PF - 2, T - 1 - t);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (loader)
+                wait_vmcnt_steps<L, PF>(after);
+            else
+                wait_vmcnt_steps<LB, PF>(after);
+            meet();
+            if (t >= 1 && t - 1 + PF < T) issue((t - 1) % PF);
+            compute(t % PF);
+        }
+    } else {
     // whole rounds: every slot is refilled right after it is read, as long as
     // steps remain (no load is issued that the wave does not consume, so the
     // last step's wait is the wave's last).  The rounds in which every step
@@ -1183,6 +1236,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
             if (t0 + i < T) step(i, T - 1 - (t0 + i));
             if (t0 + i + PF < T) issue(i);
         }
+    }
     }
     // no LDS write may still be on its way when the workgroup's LDS is reused
     wait_vmcnt<0>();

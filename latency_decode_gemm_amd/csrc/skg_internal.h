@@ -130,6 +130,9 @@ KernelPtr valu_kernel_ga(int M, int variant);  // activations from global memory
 KernelPtr mfma_kernel_mt2(int inner, int row_tiles, int depth);
 KernelPtr mfma_kernel_mt3(int inner, int row_tiles, int depth);
 KernelPtr mfma_kernel_mt4(int inner, int row_tiles, int depth);
+// LDS-ring kernels with a barrier every K step, M <= 16 (skg_mfma_sync.hip);
+// nullptr for other kinds or where a combination is not built
+KernelPtr mfma_kernel_sync(int inner, int M, int row_tiles, int depth);
 // tokens the VALU kernels (and so the fp32-weight path) take at most
 constexpr int kMaxMValu = 16;
 // the same three tables over fp32 weights (skg_f32w_lo/hi/ga.hip)

@@ -139,6 +139,8 @@ KernelPtr find_kernel(int inner, int M, int row_tiles, int depth, bool f32w) {
         return nullptr;
     }
     if (f32w) return nullptr;  // matrix-core kernels take bf16 weights only
+    if (inner == SKG_INNER_MFMA_RING_SYNC || inner == SKG_INNER_MFMA_RING_SHARED)
+        return mfma_kernel_sync(inner, M, row_tiles, depth);
     if (M > 16) {  // several token tiles of 16
         const int mt = (M + 15) / 16;
         return mt == 2   ? mfma_kernel_mt2(inner, row_tiles, depth)

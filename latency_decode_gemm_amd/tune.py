@@ -382,9 +382,11 @@ def main():
             odt = skg.SKG_OUT_BF16 if out == "bf16" else skg.SKG_OUT_F32
             C = torch.zeros((M, ldc), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                             device="cuda")
-            inner_set = ([0, 3] if M < 2 or f32w else [0, 3, 1, 2, 4, 5] if M <= 8 else
-                         [0, 1, 2, 4, 5] if M <= 12 else [1, 2, 4, 5, 0] if M <= 16 else
-                         [1, 2, 4, 5])
+            # (6, 7: the LDS ring with a barrier every step, and with the
+            # activation tile shared by the workgroup's waves; M <= 16)
+            inner_set = ([0, 3] if M < 2 or f32w else [0, 3, 1, 2, 4, 5, 6, 7] if M <= 8 else
+                         [0, 1, 2, 4, 5, 6, 7] if M <= 12 else
+                         [1, 2, 4, 5, 6, 7, 0] if M <= 16 else [1, 2, 4, 5])
             cands = structures(skg, M, K, N, inner_set, check)
             timed = {}
             print(f"M={M} K={K} N={N}: {len(cands)} stage-1 candidates", file=sys.stderr,

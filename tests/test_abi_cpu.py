@@ -106,7 +106,7 @@ def test_check_config_rules():
     assert not skg.skinny_gemm_check_config(9, 7168, 256, mk(depth=4, **ga))
     assert not skg.skinny_gemm_check_config(8, 7168, 256, mk(depth=8, **ga))
     assert skg.skinny_gemm_check_config(2, 7168, 256, mk(depth=12, **ga))
-    assert not skg.skinny_gemm_check_config(4, 7168, 256, mk(inner=6, waves_k=4))  # no such inner
+    assert not skg.skinny_gemm_check_config(4, 7168, 256, mk(inner=8, waves_k=4))  # no such inner
 
 
 def test_even_backend_rules():
@@ -202,12 +202,40 @@ def test_compiled_variant_lists_match_library():
                            (skg.SKG_INNER_MFMA, _capi.MFMA_VARIANTS),
                            (skg.SKG_INNER_MFMA_GA, _capi.MFMA_VARIANTS),
                            (skg.SKG_INNER_MFMA_RING, _capi.MFMA_VARIANTS),
-                           (skg.SKG_INNER_MFMA_RING_GA, _capi.MFMA_VARIANTS)):
+                           (skg.SKG_INNER_MFMA_RING_GA, _capi.MFMA_VARIANTS),
+                           (skg.SKG_INNER_MFMA_RING_SYNC, _capi.SYNC_VARIANTS),
+                           (skg.SKG_INNER_MFMA_RING_SHARED, _capi.SHARED_VARIANTS)):
         for rt in (1, 2, 3, 4, 8):
             for d in range(0, 10):
                 cfg = skg.SkgConfig.make(inner=inner, row_tiles=rt, depth=d, waves_k=2)
                 ok = skg.skinny_gemm_check_config(4, 1024, 512, cfg)
                 assert ok == ((rt, d) in allowed), (inner, rt, d)
+
+
+def test_barrier_kinds_rules():
+    """The barrier kinds take M <= 16 and bf16 weights; the shared
+    activation ring needs depth >= 3 and holds one activation tile per depth
+    slot and K-wave group beside the waves' weight rings (so a configuration
+    whose per-wave rings would overflow the LDS with their own activation
+    tiles can fit with the shared one)."""
+    mk = skg.SkgConfig.make
+    sync = dict(inner=skg.SKG_INNER_MFMA_RING_SYNC, split_k=1, row_tiles=1, waves_n=3,
+                waves_k=1, depth=3, rb_per_wg=2)
+    shared = dict(sync, inner=skg.SKG_INNER_MFMA_RING_SHARED)
+    for kw in (sync, shared):
+        assert skg.skinny_gemm_check_config(16, 1536, 24576, mk(**kw))
+        assert not skg.skinny_gemm_check_config(17, 1536, 24576, mk(**kw))
+        assert not skg.skinny_gemm_f32w_check_config(8, 7168, 256, mk(**kw))
+    assert skg.skinny_gemm_check_config(16, 1536, 24576, mk(**dict(sync, depth=2)))
+    assert not skg.skinny_gemm_check_config(16, 1536, 24576, mk(**dict(shared, depth=2)))
+    # 8 waves x depth 3: with per-wave activation tiles 8 x 3 x 2 x 4 KB = 192 KB;
+    # shared, 8 x 3 x 4 KB + 3 x 4 x 4 KB = 144 KB
+    big = dict(backend=skg.SKG_BACKEND_SPLITK, split_k=3, row_tiles=1, waves_n=2, waves_k=4,
+               depth=3)
+    assert not skg.skinny_gemm_check_config(16, 7168, 2112, mk(inner=skg.SKG_INNER_MFMA_RING_SYNC,
+                                                               **big))
+    assert skg.skinny_gemm_check_config(16, 7168, 2112, mk(inner=skg.SKG_INNER_MFMA_RING_SHARED,
+                                                           **big))
 
 
 def test_workspace_bytes():

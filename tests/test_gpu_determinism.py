@@ -63,6 +63,27 @@ def test_split_k_forced_is_reproducible():
                           M, 256, 1000, (M, cfg))
 
 
+def test_shared_activation_ring_repeats():
+    """The shared activation ring hands each step's tile from the loading
+    wave to the others across the step barrier; 1000 calls of it (several
+    waves on one K range, and two K-wave groups with a one-pass split) are
+    bit-identical to the first, which the float64 check also accepts."""
+    SH = skg.SKG_INNER_MFMA_RING_SHARED
+    cases = [(16, 1536, 3072, MK(inner=SH, split_k=1, row_tiles=1, waves_n=3, waves_k=1,
+                                 depth=3, rb_per_wg=2)),
+             (16, 7168, 256, MK(inner=SH, split_k=3, row_tiles=1, waves_n=2, waves_k=4,
+                                depth=3))]
+    for M, K, N, cfg in cases:
+        A_bits = inputs.make_a(M, K, N)
+        B_bits = inputs.make_b(K, N)
+        A, B = gu.operands(A_bits, B_bits, K)
+        first = skg.skinny_gemm_bf16_with_config(A, B, cfg)
+        r = gu.assess(first, A_bits, B_bits, K)
+        assert r["ok"], (cfg, r)
+        _repeat_identical(lambda out: skg.skinny_gemm_bf16_with_config(A, B, cfg, out=out),
+                          M, N, 1000, (M, K, N, cfg))
+
+
 def _repeat_identical(call, M, N, reps, what, batch=50):
     """Runs call(out) reps times, batch outputs at a time, and stops at the
     first output that differs bit for bit from the first one."""

@@ -18,6 +18,7 @@ MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 VG = skg.SKG_INNER_VALU_GA
 RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
+SY, SH = skg.SKG_INNER_MFMA_RING_SYNC, skg.SKG_INNER_MFMA_RING_SHARED
 
 FAMILIES = [
     None,  # the dispatch table's choice
@@ -46,6 +47,11 @@ FAMILIES = [
     MK(inner=RG, split_k=1, row_tiles=2, waves_n=1, waves_k=2, depth=3),
     MK(backend=skg.SKG_BACKEND_SPLITK_2PASS, inner=RG, split_k=3, row_tiles=1, waves_n=2,
        waves_k=1, depth=6),
+    MK(inner=SY, split_k=1, row_tiles=1, waves_n=3, waves_k=1, depth=3, rb_per_wg=2),
+    MK(inner=SH, split_k=1, row_tiles=1, waves_n=3, waves_k=1, depth=4, rb_per_wg=2),
+    MK(backend=skg.SKG_BACKEND_EVEN, inner=SH, split_k=1, row_tiles=2, waves_n=1, waves_k=2,
+       depth=3),
+    MK(inner=SH, split_k=3, row_tiles=1, waves_n=2, waves_k=2, depth=3),
 ]
 
 
@@ -67,8 +73,9 @@ def _fid(c):
     if c is None:
         return "dispatch"
     return ("p2_" if c.backend == 2 else "ev_" if c.backend == 3 else "") + \
-        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
-        f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}"
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga",
+         SY: "ringsync", SH: "ringshared"}[c.inner] + \
+        f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_b{c.rb_per_wg}_d{c.depth}"
 
 
 def _gemm(A, B, cfg, out_dtype):

@@ -19,6 +19,7 @@ MK = skg.SkgConfig.make
 V, F, GA = skg.SKG_INNER_VALU, skg.SKG_INNER_MFMA, skg.SKG_INNER_MFMA_GA
 VG = skg.SKG_INNER_VALU_GA
 RF, RG = skg.SKG_INNER_MFMA_RING, skg.SKG_INNER_MFMA_RING_GA
+SY, SH = skg.SKG_INNER_MFMA_RING_SYNC, skg.SKG_INNER_MFMA_RING_SHARED
 P2 = skg.SKG_BACKEND_SPLITK_2PASS
 EV = skg.SKG_BACKEND_EVEN
 
@@ -51,6 +52,10 @@ def test_workload_point(p):
     if buf is not None and buf.shape[1] > p["N"]:
         # columns [N, ldc) of the strided output are untouched (still NaN)
         assert np.isnan(gu.to_f64(buf[:, p["N"]:])).all()
+
+
+SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 777, 33),
+          (5, 7168, 100), (11, 520, 50), (2, 9, 5), (13, 33, 300)]
 
 
 def _configs():
@@ -92,16 +97,35 @@ def _configs():
                 MK(backend=EV, inner=RG, split_k=4, row_tiles=G, waves_n=1, waves_k=1, depth=PF),
                 MK(backend=EV, inner=RF, split_k=4, row_tiles=G, waves_n=1, waves_k=1, depth=PF,
                    rb_per_wg=2)]
+    # the barrier kinds: several waves on one K range (direct stores), K-wave
+    # groups (the stash; one K-wave where two do not fit the LDS with a deep
+    # ring), a one-pass and a two-pass split, rows dealt evenly
+    for (G, PF) in skg._capi.SYNC_VARIANTS:
+        for inner in (SY, SH):
+            if inner == SH and (G, PF) not in skg._capi.SHARED_VARIANTS:
+                continue
+            wk = 2 if _fits_a_shape(MK(inner=inner, split_k=1, row_tiles=G, waves_n=2,
+                                       waves_k=2, depth=PF)) else 1
+            out += [MK(inner=inner, split_k=1, row_tiles=G, waves_n=3, waves_k=1, depth=PF,
+                       rb_per_wg=2),
+                    MK(inner=inner, split_k=1, row_tiles=G, waves_n=2, waves_k=wk, depth=PF),
+                    MK(inner=inner, split_k=3, row_tiles=G, waves_n=2, waves_k=1, depth=PF),
+                    MK(backend=P2, inner=inner, split_k=2, row_tiles=G, waves_n=2, waves_k=1,
+                       depth=PF),
+                    MK(backend=EV, inner=inner, split_k=1, row_tiles=G, waves_n=2, waves_k=wk,
+                       depth=PF)]
     return out
 
 
-SHAPES = [(1, 2880, 200), (3, 1003, 77), (8, 4104, 130), (16, 2880, 128), (16, 777, 33),
-          (5, 7168, 100), (11, 520, 50), (2, 9, 5), (13, 33, 300)]
+def _fits_a_shape(cfg):
+    return any(skg.skinny_gemm_check_config(M, K, N, cfg) for (M, K, N) in SHAPES)
+
 
 
 def _cfg_id(c):
     return ("p2_" if c.backend == P2 else "ev_" if c.backend == EV else "") + \
-        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga"}[c.inner] + \
+        {V: "valu", F: "mfma", GA: "mfmaga", VG: "valuga", RF: "ring", RG: "ringga",
+         SY: "ringsync", SH: "ringshared"}[c.inner] + \
         f"_S{c.split_k}_r{c.row_tiles}_n{c.waves_n}_k{c.waves_k}_d{c.depth}_b{c.rb_per_wg}"
 
 
