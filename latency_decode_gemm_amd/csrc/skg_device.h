@@ -1054,7 +1054,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
 
     int lb = 0, lst = 0;
     const uint16_t *rowp[G][4];
-    auto set_rows = [&](int b) {
+    auto set_rows = [&](int b) __attribute__((always_inline)) {
         int bst = 0, bcnt = 1;
         if (b < w.nblk) block_rows(p, w.rb0 + b * w.rbs, bst, bcnt);
         const int rl = wn * (16 * G) + hi;
@@ -1068,7 +1068,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     };
     const uint32_t ring_addr = lds_addr_of(ring);
     const uint32_t aring_addr = lds_addr_of(aring);
-    auto issue = [&](int slot) {
+    auto issue = [&](int slot) __attribute__((always_inline)) {
         const uint32_t dst = ring_addr + slot * (NT * kTileBytes);
         const uint32_t adst =
             SH ? aring_addr + (slot * p.waves_k + wk) * kTileBytes : dst + G * kTileBytes;
@@ -1113,12 +1113,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
 
     int cb = 0, cst = 0;
     // the workgroup's waves meet (their earlier LDS reads complete first)
-    auto meet = [&]() {
+    auto meet = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot) __attribute__((always_inline)) {
         const uint4 *tl = ring + slot * (NT * 256);
         const uint4 *atl = SH ? aring + (slot * p.waves_k + wk) * (MT * 256) : tl + G * 256;
         // all operands first, so the reads go out back to back
@@ -1187,7 +1187,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
             ++cb;
         }
     };
-    auto step = [&](int slot, int left) {
+    auto step = [&](int slot, int left) __attribute__((always_inline)) {
         // this slot's loads are the oldest; the later steps (PF - 1 of them,
         // or the `left` steps still to come near the end) stay in flight
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
