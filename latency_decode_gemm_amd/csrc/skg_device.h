@@ -541,6 +541,21 @@ __device__ __forceinline__ void wait_vmcnt_steps(int r) {
     }
 }
 
+// Waits until at most min(PF - 1, r) * LB + min(PF - 2, r) * LA vector memory
+// operations are outstanding, r = min(left, R - 1) (left wave-uniform).
+template <int LB, int LA, int PF, int R>
+__device__ __forceinline__ void wait_ring_left(int left) {
+    if constexpr (R <= 1) {
+        wait_vmcnt<0>();
+    } else {
+        constexpr int r = R - 1;
+        if (left >= r)
+            wait_vmcnt<(r < PF - 1 ? r : PF - 1) * LB + (r < PF - 2 ? r : PF - 2) * LA>();
+        else
+            wait_ring_left<LB, LA, PF, R - 1>(left);
+    }
+}
+
 template <int NV>
 __device__ __forceinline__ void staged_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1005,10 +1020,11 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
 // once per workgroup (by the waves with wn == 0, one per K-wave group) into a
 // ring the waves share, instead of once per wave.  A shared slot can only be
 // refilled when every wave has read it, i.e. after the next step's barrier,
-// so with SY = 2 a step first waits for its own loads, meets the others, then
-// refills the slot the previous step used (depth >= 3 keeps depth - 2 steps
-// in flight behind the one being read).  Every wave of a workgroup runs the
-// same number of steps, so all of them reach every barrier.
+// so the shared ring runs one step behind the weights' (depth >= 3 keeps
+// depth - 2 activation steps in flight); each wave's weights are refilled
+// right after it reads them, as in the other kinds.  Every wave of a
+// workgroup runs the same number of steps, so all of them reach every
+// barrier.
 template <int G, int PF, int AQ, int MT = 1, int SY = 0>
 __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p) {
     constexpr bool AG = AQ > 0;
@@ -1070,8 +1086,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     const uint32_t aring_addr = lds_addr_of(aring);
     auto issue = [&](int slot) __attribute__((always_inline)) {
         const uint32_t dst = ring_addr + slot * (NT * kTileBytes);
-        const uint32_t adst =
-            SH ? aring_addr + (slot * p.waves_k + wk) * kTileBytes : dst + G * kTileBytes;
+        const uint32_t adst = dst + G * kTileBytes;  // the wave's own activation tiles
         const int cb0 = wv_c0 + lst * kValuStep;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1079,25 +1094,37 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
 #pragma unroll
             for (int t = 0; t < G; ++t)
                 lds_dma16_raw<true>(rowp[t][q] + off, dst + t * kTileBytes + 1024 * q);
-            if constexpr (AG) {
-                if (loader)
+            if constexpr (AG && !SH)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        if (q < AQ)
-                            lds_dma16_raw<false>(arow[mt * AQ + q] + off,
-                                                 adst + mt * kTileBytes + 1024 * q);
-            }
+                for (int mt = 0; mt < MT; ++mt)
+                    if (q < AQ)
+                        lds_dma16_raw<false>(arow[mt * AQ + q] + off,
+                                             adst + mt * kTileBytes + 1024 * q);
         }
         if (++lst == SPB) {
             lst = 0;
             set_rows(++lb);
         }
     };
+    // SY = 2, the loading waves: the activation tile of step u (its K range
+    // depends on u's place in the row block only) into shared slot u % PF
+    auto issue_a = [&](int u) __attribute__((always_inline)) {
+        const uint32_t adst = aring_addr + ((u % PF) * p.waves_k + wk) * kTileBytes;
+        const int cb0 = wv_c0 + (u % SPB) * kValuStep;
+#pragma unroll
+        for (int q = 0; q < AQ; ++q)
+            lds_dma16_raw<false>(arow[q] + window_off(cb0 + swz[q], p), adst + 1024 * q);
+    };
 
     set_rows(0);
     if constexpr (!AG) stage_a_frag<true, MT>(p, As, w.wg_c0);  // oldest loads
 #pragma unroll
-    for (int i = 0; i < PF; ++i) issue(i);
+    for (int i = 0; i < PF; ++i) {
+        issue(i);
+        // the shared ring runs one step shorter (its slot is refilled after
+        // the barrier that shows every wave has read it)
+        if (SH && loader && i < PF - 1) issue_a(i);
+    }
     if constexpr (!AG) staged_barrier<PF * L>();
 
     f32x4_t acc[G][MT];
@@ -1201,20 +1228,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     };
 
     if constexpr (SH) {
-        // refills after the barrier: step t - 1 + PF into the slot step t - 1
-        // used, so behind step t's loads there are PF - 2 steps in flight (PF
-        // - 1 at the first step), each of L loads for a loading wave, LB for
-        // the others
+        // Issue order B(0) A(0) B(1) A(1) ...: a wave's weights B(u) for step
+        // u are refilled right after it reads slot u - PF, as in the other
+        // kinds; the activations A(u) only after the barrier of step u - PF +
+        // 1.  Behind A(t) (a loading wave) there are then min(PF - 1, left)
+        // weight steps and min(PF - 2, left) activation steps, left = T - 1 -
+        // t; behind B(t) (the other waves) min(PF - 1, left) weight steps.
         for (int t = 0; t < T; ++t) {
-            const int after = t == 0 ? min(PF - 1, T - 1) : min(PF - 2, T - 1 - t);
+            const int left = T - 1 - t;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if (loader)
-                wait_vmcnt_steps<L, PF>(after);
+                wait_ring_left<LB, MT * AQ, PF, PF>(left);
             else
-                wait_vmcnt_steps<LB, PF>(after);
+                wait_ring_left<LB, 0, PF, PF>(left);
             meet();
-            if (t >= 1 && t - 1 + PF < T) issue((t - 1) % PF);
+            if (loader && t + PF - 1 < T) issue_a(t + PF - 1);
             compute(t % PF);
+            if (t + PF < T) issue(t % PF);
         }
     } else {
     // whole rounds: every slot is refilled right after it is read, as long as
