@@ -1291,13 +1291,36 @@ constexpr KernelPtr f32w_kernel() {
         return nullptr;
 }
 
+// Over bf16 weights with the activation chunks in the load ring (AG), the
+// ring holds M extra loads per step. Configurations with M * depth > 32 are
+// rejected by the configuration check, and 8 tokens with 4 rows at depth 4
+// spill to scratch (the code object's metadata report a private segment), so
+// none of these is built: the largest M per (R, PF).
+constexpr int bf16_ga_max_m(int R, int PF) {
+    return (R == 4 && PF == 4) ? 7 : (32 / PF < 8 ? 32 / PF : 8);
+}
+
+template <int M, int R, int PF>
+constexpr KernelPtr bf16_ga_kernel() {
+    if constexpr (M <= bf16_ga_max_m(R, PF))
+        return skg_valu_kernel<M, R, PF, true>;
+    else
+        return nullptr;
+}
+
 // Instantiation list for one M, in the order of kValuVariants (bf16
-// weights; SKG_VALU_ROW_F32W: fp32 weights, nullptr where not built).
+// weights, activations staged in LDS; SKG_VALU_ROW_GA: activations in the
+// ring; SKG_VALU_ROW_F32W: fp32 weights; nullptr where not built).
 #define SKG_VALU_ROW(M, AG)                                                              \
     {skg_valu_kernel<M, 1, 4, AG>, skg_valu_kernel<M, 1, 8, AG>,                         \
      skg_valu_kernel<M, 1, 12, AG>, skg_valu_kernel<M, 2, 2, AG>,                        \
      skg_valu_kernel<M, 2, 4, AG>, skg_valu_kernel<M, 2, 8, AG>,                         \
      skg_valu_kernel<M, 4, 2, AG>, skg_valu_kernel<M, 4, 4, AG>}
+#define SKG_VALU_ROW_GA(M)                                                               \
+    {bf16_ga_kernel<M, 1, 4>(), bf16_ga_kernel<M, 1, 8>(),                               \
+     bf16_ga_kernel<M, 1, 12>(), bf16_ga_kernel<M, 2, 2>(),                              \
+     bf16_ga_kernel<M, 2, 4>(), bf16_ga_kernel<M, 2, 8>(),                               \
+     bf16_ga_kernel<M, 4, 2>(), bf16_ga_kernel<M, 4, 4>()}
 #define SKG_VALU_ROW_F32W(M, AG)                                                         \
     {f32w_kernel<M, 1, 4, AG>(), f32w_kernel<M, 1, 8, AG>(),                             \
      f32w_kernel<M, 1, 12, AG>(), f32w_kernel<M, 2, 2, AG>(),                            \

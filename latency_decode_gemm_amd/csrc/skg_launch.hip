@@ -101,6 +101,17 @@ __global__ void skg_splitk_reduce_kernel(KParams p) {
     }
 }
 
+// The register ring with activations from L2 at 2 row tiles and depth 4
+// spills to scratch over one full token tile (the code object's metadata
+// report a private segment), so that combination is not built.
+template <int G, int PF>
+constexpr KernelPtr mfma_ga4_kernel() {
+    if constexpr (G == 2 && PF == 4)
+        return nullptr;
+    else
+        return skg_mfma_kernel<G, PF, 4>;
+}
+
 struct MfmaVariant {
     int G, PF;
     KernelPtr lds_a;  // activations staged in LDS
@@ -113,7 +124,7 @@ struct MfmaVariant {
      PF,                                                                                 \
      skg_mfma_kernel<G, PF, 0>,                                                          \
      skg_mfma_kernel<G, PF, 2>,                                                          \
-     skg_mfma_kernel<G, PF, 4>,                                                          \
+     mfma_ga4_kernel<G, PF>(),                                                           \
      skg_mfma_ring_kernel<G, PF, 0>,                                                     \
      skg_mfma_ring_kernel<G, PF, 2>,                                                     \
      skg_mfma_ring_kernel<G, PF, 4>}

@@ -6,9 +6,8 @@ namespace skg {
 
 KernelPtr valu_kernel_ga(int M, int variant) {
     static const KernelPtr table[8][kNumValu] = {
-        SKG_VALU_ROW(1, true), SKG_VALU_ROW(2, true), SKG_VALU_ROW(3, true),
-        SKG_VALU_ROW(4, true), SKG_VALU_ROW(5, true), SKG_VALU_ROW(6, true),
-        SKG_VALU_ROW(7, true), SKG_VALU_ROW(8, true)};
+        SKG_VALU_ROW_GA(1), SKG_VALU_ROW_GA(2), SKG_VALU_ROW_GA(3), SKG_VALU_ROW_GA(4),
+        SKG_VALU_ROW_GA(5), SKG_VALU_ROW_GA(6), SKG_VALU_ROW_GA(7), SKG_VALU_ROW_GA(8)};
     if (M < 1 || M > 8 || variant < 0 || variant >= kNumValu) return nullptr;
     return table[M - 1][variant];
 }

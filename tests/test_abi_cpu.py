@@ -407,6 +407,30 @@ def test_f32w_spilling_variants_are_not_built():
     assert skg.skinny_gemm_check_config(8, 1024, 512, ga)
 
 
+def test_bf16_spilling_variants_are_not_built():
+    """Over bf16 weights, the activation-ring VALU kernels run up to
+    M * depth = 32 tokens x steps, except 4 rows at depth 4, whose ring
+    spills at M = 8, and the register-ring MFMA kernel with 2 row tiles at
+    depth 4 is not built over a full token tile; their neighbours exist
+    (tests/test_code_objects.py checks that no built kernel spills)."""
+    mk = _capi.SkgConfig.make
+    VG = skg.SKG_INNER_VALU_GA
+    for (R, PF), top in {(1, 12): 2, (2, 8): 4, (1, 8): 4, (4, 4): 7, (1, 4): 8,
+                         (2, 2): 8}.items():
+        cfg = mk(inner=VG, row_tiles=R, depth=PF, waves_k=2)
+        assert skg.skinny_gemm_check_config(top, 1024, 512, cfg), (R, PF)
+        if top < 8:
+            assert not skg.skinny_gemm_check_config(top + 1, 1024, 512, cfg), (R, PF)
+        # the LDS-staged kernel of the same shape is built for every M
+        assert skg.skinny_gemm_check_config(16, 1024, 512, mk(inner=skg.SKG_INNER_VALU,
+                                                              row_tiles=R, depth=PF, waves_k=2))
+    ga24 = mk(inner=skg.SKG_INNER_MFMA_GA, row_tiles=2, depth=4, waves_k=1)
+    assert skg.skinny_gemm_check_config(8, 1024, 512, ga24)
+    assert not skg.skinny_gemm_check_config(9, 1024, 512, ga24)
+    assert skg.skinny_gemm_check_config(16, 1024, 512, mk(inner=skg.SKG_INNER_MFMA_RING_GA,
+                                                          row_tiles=2, depth=4, waves_k=1))
+
+
 # --- the middle tier (16 < M <= 64) ---------------------------------------------
 
 def test_mid_tier_rules():
