@@ -399,6 +399,8 @@ bool make_geometry(int M, int K, int N, const skg_config &cfg, Geometry *g) {
     // one 64-bit slot per output
     r.ws_floats = (S > 1 && !one_pass) ? (size_t)r.num_rb * S * M * r.rows_per_wg : 0;
     r.slot_words = one_pass ? (size_t)r.num_rb * (S - 1) * M * r.rows_per_wg * 2 : 0;
+    // (the kernels index the slots in 31 bits)
+    if (r.slot_words / 2 >= ((size_t)1 << 31)) return false;
     if ((int64_t)r.grid_rb * S > 0x7FFFFFFF) return false;
     *g = r;
     return true;
