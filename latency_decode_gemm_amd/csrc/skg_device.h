@@ -425,27 +425,30 @@ __device__ __forceinline__ void finish_output(const KParams &p, const WgPlan &w,
     }
 }
 
-// VALU kernels: the stash is [row block][K-wave][m][local row]; threads take
-// (token, local row) pairs, consecutive threads consecutive rows.  base(b, q,
-// rl) is the stash index of token 0 of (row block b, K-wave q, local row rl);
-// mofs(m) adds token m.
-template <class BASE, class MOFS>
+// VALU kernels (R row slots of 4 rows per wave): the stash is [row block]
+// [K-wave][m][local row].  The thread of K-wave wk, N-wave wn and lane l takes
+// local row 4 R wn + (l mod 4 R) and tokens l / (4 R) + (16 / R)(wk + waves_k
+// i): each output once, consecutive lanes on consecutive rows (conflict-free
+// stash reads, coalesced stores), and no division (the waves of a SIMD run
+// the epilogue alone after the stream, where a chain of per-thread divisions
+// cost half a microsecond).  The waves_k partials are added in K-wave order.
+// bst0 and bcnt0: the rows of the workgroup's first row block.
+template <int R>
 __device__ __forceinline__ void write_blocks(const KParams &p, const WgPlan &w, const float *stash,
-                                             BASE base, MOFS mofs) {
+                                             int bst0, int bcnt0, int wk, int wn, int lane) {
     __syncthreads();
-    const int NB = p.rows_per_wg;  // never more than the workgroup's threads
+    const int NB = p.rows_per_wg;  // 4 R waves_n
     const int M = p.M;
-    // thread -> local row rl and tokens m0, m0 + mstep, ...
-    const int m0 = threadIdx.x / NB;
-    const int rl = threadIdx.x - m0 * NB;
-    const int mstep = 64 * p.waves_n * p.waves_k / NB;
+    const int rl = 4 * R * wn + (lane & (4 * R - 1));
+    const int mstep = (16 / R) * p.waves_k;
     for (int b = 0; b < w.nblk; ++b) {
         const int rb = w.rb0 + b * w.rbs;
-        int bst, bcnt;
-        block_rows(p, rb, bst, bcnt);
-        for (int m = m0; m < M; m += mstep) {
-            float v = stash[base(b, 0, rl) + mofs(m)];
-            for (int q = 1; q < p.waves_k; ++q) v += stash[base(b, q, rl) + mofs(m)];
+        int bst = bst0, bcnt = bcnt0;
+        if (b > 0) block_rows(p, rb, bst, bcnt);
+        const float *blk = stash + b * p.waves_k * M * NB + rl;
+        for (int m = lane / (4 * R) + (16 / R) * wk; m < M; m += mstep) {
+            float v = blk[m * NB];
+            for (int q = 1; q < p.waves_k; ++q) v += blk[(q * M + m) * NB];
             finish_output(p, w, rb, bst, bcnt, m, rl, v);
         }
     }
@@ -685,6 +688,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         staged_barrier<PF * R * WL>();
     }
 
+    // rows of the first row block, for its end (computed while the first
+    // loads are on their way)
+    int bst0 = 0, bcnt0 = 0;
+    if (w.nblk > 0) block_rows(p, w.rb0, bst0, bcnt0);
+    __asm__ volatile("" : "+s"(bst0), "+s"(bcnt0));
+
     float acc[R][M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -739,8 +748,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         if (++cst == SPB) {
             // row block done: lane m of each row group now takes token m
             const int rb = w.rb0 + cb * w.rbs;
-            int bst, bcnt;
-            block_rows(p, rb, bst, bcnt);
+            int bst = bst0, bcnt = bcnt0;
+            if (cb > 0) block_rows(p, rb, bst, bcnt);
             float *dst = stash + cb * per_block + (wk * M + l16) * NB + rl0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -785,11 +794,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
 #pragma unroll
     for (int i = 0; i < PF; ++i)
         if (t0 + i < T) step(buf[i], abuf[i]);
-    if (!direct)
-        write_blocks(
-            p, w, stash,
-            [&](int b, int q, int rl) { return (b * p.waves_k + q) * M * NB + rl; },
-            [&](int m) { return m * NB; });
+    if (!direct) write_blocks<R>(p, w, stash, bst0, bcnt0, wk, wn, lane);
 }
 
 // ---- MFMA kernel ------------------------------------------------------------
