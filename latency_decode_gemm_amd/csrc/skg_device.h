@@ -156,11 +156,13 @@ __device__ __forceinline__ float dot8_f32w(const uint4 &a, const uint4 &w0, cons
 }
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+// (both results formed and one selected: no branch per value in the
+// epilogues, where one wave per SIMD runs them back to back)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x0040u;
+    return (uint16_t)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet_nan : rounded);
 }
 
 __device__ __forceinline__ void store_c(const KParams &p, int m, int n, float v) {
@@ -169,6 +171,25 @@ __device__ __forceinline__ void store_c(const KParams &p, int m, int n, float v)
         reinterpret_cast<uint16_t *>(p.C)[off] = f32_to_bf16_rne(v);
     else
         reinterpret_cast<float *>(p.C)[off] = v;
+}
+
+// The outputs of one accumulator fragment lane: tokens m0 .. m0 + 3 (those
+// below M) of column n, the output type tested once and the rows of C
+// reached by adding ldc.
+__device__ __forceinline__ void store_c4(const KParams &p, int m0, int n, const f32x4_t &v) {
+    const int64_t ld = p.ldc;
+    const int64_t off = (int64_t)m0 * ld + n;
+    if (p.out_bf16) {
+        uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + off;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (m0 + j < p.M) c[j * ld] = f32_to_bf16_rne(v[j]);
+    } else {
+        float *c = reinterpret_cast<float *>(p.C) + off;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (m0 + j < p.M) c[j * ld] = v[j];
+    }
 }
 
 // ---- K tail ------------------------------------------------------------------
@@ -546,13 +567,7 @@ __device__ __forceinline__ void write_block_kwave0(const KParams &p, const f32x4
             f32x4_t v = src[(t * MT + mt) * 64];
             for (int q = 1; q < p.waves_k; ++q) v += src[q * per_q + (t * MT + mt) * 64];
             const int rl = rlw + 16 * t;
-            if (rl < bcnt) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = 16 * mt + 4 * (lane >> 4) + j;
-                    if (m < p.M) store_c(p, m, bst + rl, v[j]);
-                }
-            }
+            if (rl < bcnt) store_c4(p, 16 * mt + 4 * (lane >> 4), bst + rl, v);
         }
     }
 }
@@ -1013,16 +1028,15 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_kernel(KParams p) {
                         int ln = lane;
                         __asm__ volatile("" : "+v"(ln));
                         const int rl = rlw + 16 * t + (ln & 15);
+                        if (p.split_k == 1) {
+                            if (rl < bcnt) store_c4(p, 16 * mt + 4 * (ln >> 4), bst + rl, acc[t][mt]);
+                        } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int m = 16 * mt + 4 * (ln >> 4) + v;
-                            if (m < M) {
-                                if (p.split_k == 1) {
-                                    if (rl < bcnt) store_c(p, m, bst + rl, acc[t][mt][v]);
-                                } else {
+                            for (int v = 0; v < 4; ++v) {
+                                const int m = 16 * mt + 4 * (ln >> 4) + v;
+                                if (m < M)
                                     p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] =
                                         acc[t][mt][v];
-                                }
                             }
                         }
                     }
@@ -1252,16 +1266,15 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
                         int ln = lane;
                         __asm__ volatile("" : "+v"(ln));
                         const int rl = rlw + 16 * t + (ln & 15);
+                        if (p.split_k == 1) {
+                            if (rl < bcnt) store_c4(p, 16 * mt + 4 * (ln >> 4), bst + rl, acc[t][mt]);
+                        } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int m = 16 * mt + 4 * (ln >> 4) + v;
-                            if (m < M) {
-                                if (p.split_k == 1) {
-                                    if (rl < bcnt) store_c(p, m, bst + rl, acc[t][mt][v]);
-                                } else {
+                            for (int v = 0; v < 4; ++v) {
+                                const int m = 16 * mt + 4 * (ln >> 4) + v;
+                                if (m < M)
                                     p.ws[((size_t)(rb * p.split_k + w.s) * M + m) * NB + rl] =
                                         acc[t][mt][v];
-                                }
                             }
                         }
                     }
