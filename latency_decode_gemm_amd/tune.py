@@ -48,8 +48,13 @@ def structures(skg, M, K, N, inner_set, check=None):
     # workgroup streams few steps)
     valu_d = {1: (4, 8), 2: (2, 4), 4: (2, 4)}
     mfma_d = {1: (2, 4), 2: (1, 2), 4: (1, 2)}
+    # the barrier kinds: the shared activation ring needs depth >= 3 (and
+    # depth 4 with many waves rarely fits the LDS), so both take depth 3 too
+    sync_d = {1: (2, 3, 4), 2: (2, 3), 4: ()}
+    shared_d = {1: (3, 4), 2: (3,), 4: ()}
     for inner in inner_set:
-        depths = valu_d if inner in (0, 3) else mfma_d
+        depths = (valu_d if inner in (0, 3) else sync_d if inner == 6 else
+                  shared_d if inner == 7 else mfma_d)
         for rt, d in [(rt, d) for rt in (1, 2, 4) for d in depths[rt]]:
             for (wn, wk) in WAVES:
                 nb = rows_per_wave(inner, rt) * wn
