@@ -68,11 +68,40 @@ KERNEL_SOURCES = ["skg_device.h", "skg_internal.h", "skg_launch.hip", "skg_valu_
 F32W_SUFFIX = "_w32"  # point names of the fp32-weight router GEMM
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without its comments and with each run of whitespace made
+    one space (string and character literals kept as written), so that
+    editing a comment does not count as changing a kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored): the
+    HBM counters in profiles/traffic.json hold for the code they were taken
+    with."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "latency_decode_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "latency_decode_gemm_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -703,8 +703,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_valu_kernel(KParams p) {
         staged_barrier<PF * R * WL>();
     }
 
-    // rows of the first row block, for its end (computed while the first
-    // loads are on their way)
+    // rows of the first row block, for its end, computed while the first
+    // loads are on their way: the empty statement keeps the compiler from
+    // moving the division to the end of the stream, and holds the two
+    // (workgroup-uniform) values in scalar registers meanwhile
     int bst0 = 0, bcnt0 = 0;
     if (w.nblk > 0) block_rows(p, w.rb0, bst0, bcnt0);
     __asm__ volatile("" : "+s"(bst0), "+s"(bcnt0));
@@ -1204,8 +1206,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) skg_mfma_ring_kernel(KParams p
     const int st_block = p.waves_k * p.waves_n * G * MT * 64;
     const bool direct = direct_write(p);
     const int rlw = wn * (16 * G);
-    // rows of the first row block, for its end (computed while the first
-    // loads are on their way)
+    // rows of the first row block, for its end, computed while the first
+    // loads are on their way: the empty statement keeps the compiler from
+    // moving the division to the end of the stream, and holds the two
+    // (workgroup-uniform) values in scalar registers meanwhile
     int bst0 = 0, bcnt0 = 0;
     if (w.nblk > 0) block_rows(p, w.rb0, bst0, bcnt0);
     __asm__ volatile("" : "+s"(bst0), "+s"(bcnt0));
