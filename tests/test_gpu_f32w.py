@@ -2,7 +2,8 @@
 oracle, element by element (GPU).
 
 * the router shapes (K = 7168, N in {256, 384}, M in {1, 2, 3, 4, 8, 16}) at
-  full size with the dispatched configuration;
+  full size with the dispatched configuration, and every M = 1..16 on them
+  (the untuned M take the entry of the next larger tuned M);
 * every VALU variant and backend forced through the explicit-config entry on
   shapes with ragged K and N tails, NaN-padded leading dimensions;
 * exact cases: one-hot activation rows select fp32 weights bit for bit (any
@@ -41,6 +42,23 @@ def test_router_f32w_point(p):
     torch.cuda.synchronize()
     r = gu.assess_f32w(C, A_bits, W, K)
     assert r["ok"], r
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("N", [256, 384])
+def test_router_f32w_every_m(N, M):
+    torch = gu.torch_cuda()
+    K = 7168
+    A_bits = inputs.make_a(M, K, N)
+    W = inputs.make_w_f32(K, N)
+    A, Wd = gu.operands_f32w(A_bits, W, K)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    cfg = skg.skinny_gemm_f32w_dispatch(M, K, N)
+    print(f"M={M} K={K} N={N} cfg={cfg.as_tuple()}", flush=True)
+    skg.skinny_gemm_f32w(A, Wd, out=C)
+    torch.cuda.synchronize()
+    r = gu.assess_f32w(C, A_bits, W, K)
+    assert r["ok"], (M, N, cfg.as_tuple(), r)
 
 
 def _configs():
